@@ -1,0 +1,133 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pin suite rejects every one of them.
+
+Each mutation is an exact text replacement in one oracle source file; the
+mutated package is written to a temporary directory and imported under a
+fresh name.  A mutation whose anchor text is missing fails the test, so the
+list cannot silently drift away from the oracle's source.
+"""
+
+import importlib.util
+import pathlib
+import shutil
+import sys
+import uuid
+
+import pytest
+
+from tests import pins
+
+ORACLE_DIR = pathlib.Path(__file__).resolve().parent.parent / "oracle"
+
+# (id, file, anchor text, replacement)
+MUTANTS = [
+    # --- dense definition -------------------------------------------------
+    ("top_left_causal", "dense.py",
+     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j <= row_ids[:, None]"),
+    ("strict_causal", "dense.py",
+     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j < (row_ids[:, None] + (nk - nq))"),
+    ("causal_offset_sign", "dense.py",
+     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j <= (row_ids[:, None] + (nq - nk))"),
+    ("klen_off_by_one", "dense.py",
+     "ok = np.broadcast_to(j < limit,", "ok = np.broadcast_to(j <= limit,"),
+    ("klen_ignored", "dense.py",
+     "limit = nk if k_len_b is None else min(max(int(k_len_b), 0), nk)", "limit = nk"),
+    ("scale_dropped", "dense.py",
+     "s = (q @ k.T) * float(scale)", "s = (q @ k.T)"),
+    ("scale_squared", "dense.py",
+     "s = (q @ k.T) * float(scale)", "s = (q @ k.T) * float(scale) ** 2"),
+    ("bias_sign", "dense.py",
+     "s = s + np.asarray(bias, dtype=np.float64)", "s = s - np.asarray(bias, dtype=np.float64)"),
+    ("bias_scaled", "dense.py",
+     "s = s + np.asarray(bias, dtype=np.float64)",
+     "s = s + float(scale) * np.asarray(bias, dtype=np.float64)"),
+    ("bias_dropped", "dense.py",
+     "s = s + np.asarray(bias, dtype=np.float64)", "s = s"),
+    ("max_shift_sign", "dense.py",
+     "e = np.where(ok, np.exp(s - m[:, None]), 0.0)", "e = np.where(ok, np.exp(s + m[:, None]), 0.0)"),
+    ("mask_not_applied_to_exp", "dense.py",
+     "e = np.where(ok, np.exp(s - m[:, None]), 0.0)",
+     "e = np.exp(np.where(ok, s, np.where(np.isfinite(s), s, 0.0) * 0.0) - m[:, None])"),
+    ("no_normalisation", "dense.py",
+     "p = e / safe_ell[:, None]", "p = e"),
+    ("normalise_by_count", "dense.py",
+     "p = e / safe_ell[:, None]", "p = e / np.maximum(ok.sum(axis=1), 1)[:, None]"),
+    ("lse_drops_max", "dense.py",
+     "lse = np.where(nonempty, m + np.log(safe_ell), -np.inf)",
+     "lse = np.where(nonempty, np.log(safe_ell), -np.inf)"),
+    ("lse_log2", "dense.py",
+     "lse = np.where(nonempty, m + np.log(safe_ell), -np.inf)",
+     "lse = np.where(nonempty, m + np.log2(safe_ell), -np.inf)"),
+    ("empty_lse_zero", "dense.py",
+     "lse = np.where(nonempty, m + np.log(safe_ell), -np.inf)",
+     "lse = np.where(nonempty, m + np.log(safe_ell), 0.0)"),
+    ("empty_row_nan", "dense.py",
+     "o[~nonempty] = 0.0", "o[~nonempty] = np.nan"),
+    ("values_transposed_rows", "dense.py",
+     "o = p @ v", "o = p @ v[::-1]"),
+    ("keys_reversed", "dense.py",
+     "s = (q @ k.T) * float(scale)", "s = (q @ k[::-1].T) * float(scale)"),
+    ("row_ids_ignored", "dense.py",
+     "ok = allowed_mask(row_ids, nq, nk, causal, k_len_b)",
+     "ok = allowed_mask(np.arange(rows), nq, nk, causal, k_len_b)"),
+    # --- tile recurrence and merge ------------------------------------------
+    ("rescale_l_only", "online.py",
+     "u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]", "u[r] = u[r] + e @ v[ka:kb][ok[r]]"),
+    ("rescale_u_only", "online.py",
+     "ell[r] = alpha * ell[r] + e.sum()", "ell[r] = ell[r] + e.sum()"),
+    ("alpha_inverted", "online.py",
+     "alpha = np.exp(m[r] - m_new) if ell[r] > 0 else 0.0",
+     "alpha = np.exp(m_new - m[r]) if ell[r] > 0 else 0.0"),
+    ("tile_local_softmax_sum", "online.py",
+     "u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]",
+     "u[r] = u[r] + (e @ v[ka:kb][ok[r]]) / e.sum() * ell[r]"),
+    ("tile_local_positions", "online.py",
+     "ok = allowed_mask(np.arange(qa, qb), nq, nk, causal,\n                              k_len_b)[:, ka:kb]",
+     "ok = allowed_mask(np.arange(qb - qa), qb - qa, kb - ka, causal,\n                              k_len_b)"),
+    ("bias_tile_misaligned", "online.py",
+     "s = s + np.asarray(bias, dtype=np.float64)[qa:qb, ka:kb]",
+     "s = s + np.asarray(bias, dtype=np.float64)[qa:qb, :kb - ka]"),
+    ("empty_tile_not_skipped", "online.py",
+     "if not ok[r].any():\n                    continue", "if False:\n                    continue"),
+    ("duplicates_allowed", "online.py",
+     "if np.any(seen != 1):", "if np.any(seen < 1):"),
+    ("lse_drops_max_online", "online.py",
+     "lse[qa:qb][nonempty] = m[nonempty] + np.log(ell[nonempty])",
+     "lse[qa:qb][nonempty] = np.log(ell[nonempty])"),
+    ("merge_rescale_dropped", "online.py",
+     "return m, alpha_a * l_a + alpha_b * l_b, alpha_a * u_a + alpha_b * u_b",
+     "return m, alpha_a * l_a + alpha_b * l_b, u_a + u_b"),
+    ("merge_alpha_sign", "online.py",
+     "alpha_b = np.exp(m_b - m)", "alpha_b = np.exp(m - m_b)"),
+    ("block_state_unshifted", "online.py",
+     "e = np.exp(x - m)\n    return m, e.sum(), e @ vals", "e = np.exp(x)\n    return m, e.sum(), e @ vals"),
+    ("block_state_normalised", "online.py",
+     "return m, e.sum(), e @ vals", "return m, e.sum(), (e @ vals) / e.sum()"),
+]
+
+
+def _load_mutant(tmp_path, fname, anchor, repl):
+    pkg_name = f"oracle_mut_{uuid.uuid4().hex[:8]}"
+    dst = tmp_path / pkg_name
+    shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__", "*.so", "*.o"))
+    src = (dst / fname).read_text()
+    assert src.count(anchor) == 1, f"anchor not found exactly once in {fname}: {anchor!r}"
+    (dst / fname).write_text(src.replace(anchor, repl))
+    spec = importlib.util.spec_from_file_location(pkg_name, dst / "__init__.py",
+                                                  submodule_search_locations=[str(dst)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[pkg_name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("mid,fname,anchor,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_rejected(tmp_path, mid, fname, anchor, repl):
+    mod = _load_mutant(tmp_path, fname, anchor, repl)
+    failed = pins.failing_pins(mod)
+    assert failed, f"mutant {mid} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    mod = _load_mutant(tmp_path, "dense.py", "import numpy as np", "import numpy as np")
+    assert pins.failing_pins(mod) == []
