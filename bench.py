@@ -1,0 +1,352 @@
+"""Benchmark of the attention forward library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long|decode]
+                    [--no-cpu-baseline] [--only] [--copy-calibration]
+
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in device memory: one fa_fwd call for the prefill and
+long-context workloads, one fa_decode_splitk call (partial + merge kernels)
+for decode.  W untimed steps, then exactly K timed steps between device
+synchronisations; the JSON line on stdout reports the main workload
+(default: causal bf16 prefill 4x32x4096^2, d=128) and, under "secondary",
+the long-context and decode workloads measured the same way.
+
+Algorithmic work (what the method must do, not what a kernel happens to do):
+* prefill / long: FLOPs = 2 (dk + dv) x (number of allowed query-key pairs);
+  exponentials and maxima are not counted;
+* decode: bytes = the K/V rows actually read (sum over sequences of
+  H * k_len * (dk + dv) * 2) + q + o (2 bytes each) + lse (4 bytes); the
+  split-K workspace is not counted.
+
+roofline.achieved divides that work per launch by the kernel's mean duration
+measured with HIP events recorded on the launch stream around every timed
+launch.  roofline.traffic comes from a stored rocprofv3 counter summary
+(profiles/<workload>_traffic.json) and is reported only while the kernel
+sources still hash to the value recorded with it.
+
+cpu_baseline times the float64 oracle (test infrastructure, used here only
+for this leg) on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import platform
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk (dense bf16 MFMA) x 2.4 GHz (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0      # HBM3E, published 8 TB/s
+METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s (% peak)"
+KERNEL_SOURCES = ["online_softmax_05_amd/csrc/fa_fwd_bf16.hip", "online_softmax_05_amd/csrc/fa_decode.hip",
+                  "online_softmax_05_amd/csrc/fa_common.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def causal_pairs(nq, nk):
+    """Allowed (query, key) pairs of one head under bottom-right causal."""
+    total = 0
+    for i in range(nq):
+        total += max(0, min(nk, i + nk - nq + 1))
+    return total
+
+
+def stored_traffic(name):
+    p = ROOT / "profiles" / f"{name}_traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text())
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def time_launches(fn, steps, warmup):
+    """W untimed calls, then K timed calls between synchronisations; events on
+    the current stream around each call give the per-launch duration."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(s.elapsed_time(e) for s, e in ev)
+    return dict(ms_per_step=wall * 1e3 / steps, launch_ms_mean=sum(durs) / len(durs),
+                launch_ms_median=durs[len(durs) // 2], launch_ms_min=durs[0])
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle, on a bounded sample)
+# ---------------------------------------------------------------------------
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_prefill(inp, name, budget_s):
+    import numpy as np
+
+    import oracle
+
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    scale = float(np.float32(inp["scale"]))
+    flops = 0.0
+    heads = 0
+    elapsed = 0.0  # oracle time only; device-to-host copies of the inputs are excluded
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        qh = q[b, h].double().cpu().numpy()
+        kh = k[b, h].double().cpu().numpy()
+        vh = v[b, h].double().cpu().numpy()
+        ts = time.perf_counter()
+        for r0 in range(0, N, 2048):
+            r1 = min(N, r0 + 2048)
+            oracle.attention_head(qh[r0:r1], kh, vh, scale=scale, nq=N, causal=True,
+                                  row_ids=np.arange(r0, r1))
+        elapsed += time.perf_counter() - ts
+        flops += 2.0 * (dk + dv) * causal_pairs(N, N)
+        heads += 1
+        if elapsed >= budget_s:
+            break
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"{heads} of {B * H} heads of the {name} workload, every query row, dense float64 "
+                       f"numpy oracle, {elapsed:.1f} s of oracle time (input copies excluded)",
+                seconds=elapsed, cpu=platform.processor() or platform.machine())
+
+
+def cpu_baseline_decode(inp, budget_s):
+    import numpy as np
+
+    import oracle
+
+    q, k, v, kl = inp["q"], inp["k"], inp["v"], inp["k_len_host"]
+    B, H, dk = q.shape
+    dv = v.shape[3]
+    scale = float(np.float32(inp["scale"]))
+    nbytes = 0.0
+    pairs = 0
+    elapsed = 0.0  # oracle time only; device-to-host copies of the inputs are excluded
+    for b in range(B):
+        n = int(kl[b])
+        kb = k[b, :, :n].double().cpu().numpy()
+        vb = v[b, :, :n].double().cpu().numpy()
+        qb = q[b].double().cpu().numpy()
+        ts = time.perf_counter()
+        for h in range(H):
+            oracle.attention_head(qb[h][None], kb[h], vb[h], scale=scale, nq=1)
+            nbytes += n * (dk + dv) * 2 + dk * 2 + dv * 2 + 4
+            pairs += 1
+        elapsed += time.perf_counter() - ts
+        if elapsed >= budget_s:
+            break
+    return dict(value=nbytes / elapsed / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle",
+                sample=f"{pairs} of {B * H} (sequence, head) query rows of the decode workload, dense "
+                       f"float64 numpy oracle, {elapsed:.1f} s of oracle time (input copies excluded)",
+                seconds=elapsed, cpu=platform.processor() or platform.machine())
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def run_prefill(name, args, dev):
+    import torch
+
+    import online_softmax_05_amd as fa
+    import workloads
+
+    log(f"{name}: drawing inputs on the device")
+    inp = getattr(workloads, name)(dev)
+    s = workloads.SHAPES[name]
+    B, H, N, dk, dv = s["B"], s["H"], s["Nq"], s["dk"], s["dv"]
+    out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"],
+                  out=out, lse=lse)
+
+    log(f"{name}: timing {args.warmup} + {args.steps} steps")
+    t = time_launches(step, args.steps, args.warmup)
+    pairs = B * H * causal_pairs(N, N)
+    flops = 2.0 * (dk + dv) * pairs
+    value = flops / (t["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (t["launch_ms_mean"] * 1e-3) / 1e12
+    traffic = stored_traffic(name)
+    res = dict(
+        workload=workloads.DESCRIPTIONS[name], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
+        frac_of_peak=value / PEAK_BF16_TFLOPS,
+        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
+                      kernel="fwd_bf16_kernel<128,128,64,false>", launch_ms_mean=t["launch_ms_mean"],
+                      launch_ms_median=t["launch_ms_median"], algorithmic_flops_per_launch=flops,
+                      algorithmic_bytes_per_launch=2 * B * H * N * (2 * dk + dv) + 2 * B * H * N * dv
+                      + 4 * B * H * N),
+        config=dict(workload=workloads.DESCRIPTIONS[name], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
+                    dtype="bf16", block_n=64 if inp["block_n"] == 0 else inp["block_n"],
+                    allowed_pairs=pairs),
+    )
+    if not args.no_cpu_baseline:
+        log(f"{name}: timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, name, args.cpu_budget)
+        res["cpu_baseline"]["value_same_unit_as_gpu"] = True
+    del inp, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(args, dev):
+    import torch
+
+    import online_softmax_05_amd as fa
+    import workloads
+
+    log("decode: drawing inputs on the device")
+    inp = workloads.decode(dev)
+    s = workloads.SHAPES["decode"]
+    B, H, Nk, dk, dv = s["B"], s["H"], s["Nk"], s["dk"], s["dv"]
+    chunk = inp["chunk"]
+    ws = torch.empty(fa.fa_decode_splitk_workspace_bytes(B, H, Nk, dv, chunk) // 4, dtype=torch.float32,
+                     device=dev)
+    out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_decode_splitk(inp["q"], inp["k"], inp["v"], inp["k_len"], scale=inp["scale"], chunk=chunk,
+                            out=out, lse=lse, workspace=ws)
+
+    log(f"decode: timing {args.warmup} + {args.steps} steps")
+    t = time_launches(step, args.steps, args.warmup)
+    kl = inp["k_len_host"].long()
+    nbytes = float(H * kl.sum().item() * (dk + dv) * 2 + B * H * (dk * 2 + dv * 2 + 4))
+    value = nbytes / (t["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (t["launch_ms_mean"] * 1e-3) / 1e9
+    res = dict(
+        workload=workloads.DESCRIPTIONS["decode"], value=value, unit="GB/s", ms_per_step=t["ms_per_step"],
+        frac_of_peak=value / PEAK_HBM_GBS,
+        roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
+                      traffic=stored_traffic("decode"), kernel="decode_partial_kernel + decode_merge_kernel",
+                      launch_ms_mean=t["launch_ms_mean"], launch_ms_median=t["launch_ms_median"],
+                      algorithmic_bytes_per_launch=nbytes),
+        config=dict(workload=workloads.DESCRIPTIONS["decode"], B=B, H=H, Nk_max=Nk, dk=dk, dv=dv, chunk=chunk,
+                    dtype="bf16", k_len_sum=int(kl.sum().item())),
+    )
+    if not args.no_cpu_baseline:
+        log("decode: timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_budget)
+    del inp, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_calibration(dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, to scale the HBM byte counters."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                      "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=["prefill", "long", "decode"], default="prefill")
+    ap.add_argument("--only", action="store_true", help="measure only the main workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU kernel is the unit of work; sharding is a design note).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import online_softmax_05_amd as fa
+
+    fa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+
+    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode") if w != args.workload])
+    results = {}
+    for w in order:
+        results[w] = run_decode(args, dev) if w == "decode" else run_prefill(w, args, dev)
+
+    main_res = results[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": main_res["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, drawn on the device; no dataset)",
+        "config": main_res["config"],
+        "frac_of_peak": main_res["frac_of_peak"],
+        "roofline": main_res["roofline"],
+        "cpu_baseline": main_res.get("cpu_baseline"),
+        "secondary": [dict(results[w]) for w in order[1:]],
+        "kernel_source_hash": kernel_source_hash(),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

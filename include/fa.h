@@ -1,0 +1,148 @@
+/*
+ * fa.h -- C ABI of the exact attention forward library (libfa.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for every batch entry b, head h and query row i,
+ *
+ *     s_ij  = scale * (q_i . k_j) + bias_ij          for keys j in J_i
+ *     o_i   = sum_j softmax_j(s_i.) v_j,  lse_i = ln sum_{j in J_i} exp(s_ij)
+ *
+ * tile by tile with the per-row running state (max m, denominator l,
+ * unnormalised weighted value sum u); l and u are both rescaled by
+ * exp(m_old - m_new) when the maximum rises and each row is divided once at
+ * the end.  S and P never reach device memory.  Sources, cited by title and
+ * section:
+ *   [GS] "How Does FlashAttention Preserve Global Softmax Across Tiles?"
+ *   [VW] "Flash attention and efficient attention: Visual walkthrough"
+ *   [OA] "Reducing Memory Traffic with Output Accumulation in FlashAttention"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, contiguous, last dimension fastest:
+ *   [B, H, N, d] for Q/K/V/O, [B, H, Nq] for lse, [B, H, Nq, Nk] for bias.
+ * - Every pointer argument is DEVICE memory owned by the caller.  The library
+ *   never allocates, frees or synchronises; it only enqueues kernels on
+ *   `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   Kernel faults surface at the caller's next synchronisation.
+ * - Validation happens on the host before any launch; on failure nothing is
+ *   launched and nothing is written, and the return value is a nonzero
+ *   fa_status.  Values inside device arrays (k_len) are not validated: the
+ *   kernels clamp them to [0, Nk].
+ * - The allowed key set J_i ([GS] sections 1 and 6) is the intersection of
+ *   the key-length mask j < clamp(k_len[b], 0, Nk) and, if causal, the
+ *   bottom-right causal mask j <= i + Nk - Nq (zero-based, the ends of the two
+ *   sequences aligned).  A row whose J_i is empty gets o_i = 0 and
+ *   lse_i = -inf exactly ([GS] section 6); no NaN is produced.
+ * - Inputs are assumed finite ([GS] section 1).  Accumulation is fp32 for
+ *   both dtypes; bf16 inputs use bf16 MFMA products (P is rounded to bf16
+ *   before P.V), fp32 inputs use fp32 MFMA.
+ * - The library is stateless and reentrant.
+ */
+#ifndef ONLINE_SOFTMAX_FA_H
+#define ONLINE_SOFTMAX_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O.  bias and lse are always fp32. */
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
+                             or too large for 32-bit grid/index arithmetic   */
+  FA_ERR_UNSUPPORTED = 3, /* dtype, head dim (> 128), block_n, chunk, causal
+                             flag or scale outside what the kernels support  */
+  FA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small          */
+  FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
+} fa_status;
+
+/*
+ * fa_fwd -- prefill / general forward pass ([GS] sections 1, 5-7; [OA]
+ * "Completing the Output by Traversing Tiles").
+ *
+ *   q     [B, H, Nq, dk]  dtype        read only
+ *   k     [B, H, Nk, dk]  dtype        read only (may be NULL if Nk == 0)
+ *   v     [B, H, Nk, dv]  dtype        read only (may be NULL if Nk == 0)
+ *   bias  [B, H, Nq, Nk]  fp32 or NULL; added after scaling, before masking;
+ *                                      must be finite at allowed positions
+ *   k_len [B] int32 or NULL (NULL: every sequence has Nk keys)
+ *   o     [B, H, Nq, dv]  dtype        written in full
+ *   lse   [B, H, Nq] fp32 or NULL      natural-log log-sum-exp per row
+ *   1 <= dk, dv <= 128; B, H, Nq, Nk >= 0.  B*H*Nq == 0 is a no-op (FA_OK,
+ *   pointers may then be NULL).  Nk == 0 yields o = 0, lse = -inf.
+ *   scale : finite; the usual value is 1/sqrt(dk) (computed by the caller).
+ *   causal: 0 or 1 (bottom-right alignment).
+ *   block_n: key-tile width; 0 = automatic, or 32, 64, 128.  The result does
+ *   not depend on it beyond rounding ([GS] section 9).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, const float* bias,
+           const int32_t* k_len, void* o, float* lse, int B, int H, int Nq,
+           int Nk, int dk, int dv, int dtype, float scale, int causal,
+           int block_n, void* stream);
+
+/* Host-only validation of fa_fwd's arguments (no pointer is dereferenced and
+ * no GPU is touched).  Returns the status fa_fwd would return before
+ * launching. */
+int fa_check_fwd(const void* q, const void* k, const void* v,
+                 const float* bias, const int32_t* k_len, const void* o,
+                 const float* lse, int B, int H, int Nq, int Nk, int dk,
+                 int dv, int dtype, float scale, int causal, int block_n);
+
+/*
+ * Bytes of fp32 workspace fa_decode_splitk needs:
+ *   B * H * ceil(Nk_max / chunk) * (dv + 2) * 4.
+ * Returns 0 for invalid arguments (negative sizes, chunk not a positive
+ * multiple of 64).
+ */
+size_t fa_decode_splitk_workspace_bytes(int B, int H, int Nk_max, int dv,
+                                        int chunk);
+
+/*
+ * fa_decode_splitk -- single-token decode against a KV cache, split over
+ * key chunks ([GS] section 8, split KV loading for short queries; the
+ * per-chunk states are merged with the rule of [GS] section 4 / [VW] Step 5).
+ *
+ *   q       [B, H, dk]         dtype   (one query token per sequence)
+ *   k_cache [B, H, Nk_max, dk] dtype   only keys j < k_len[b] are read
+ *   v_cache [B, H, Nk_max, dv] dtype
+ *   k_len   [B] int32, required; clamped to [0, Nk_max]
+ *   o       [B, H, dv] dtype; lse [B, H] fp32 or NULL
+ *   chunk   keys per partial state: a positive multiple of 64 (512 usual)
+ *   workspace: device buffer of at least
+ *              fa_decode_splitk_workspace_bytes(B, H, Nk_max, dv, chunk)
+ *              bytes, 16-byte aligned; its contents on entry are ignored.
+ * Two kernels are enqueued on `stream`: one partial state (m_c, l_c, u_c)
+ * per (b, h, chunk) with chunk < ceil(k_len[b] / chunk), then one merge per
+ * (b, h) in ascending chunk order.  A sequence with k_len = 0 gets o = 0,
+ * lse = -inf.
+ */
+int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* k_len, void* o, float* lse, int B, int H,
+                     int Nk_max, int dk, int dv, int chunk, int dtype,
+                     float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Host-only validation of fa_decode_splitk's arguments. */
+int fa_check_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* k_len, const void* o, const float* lse,
+                    int B, int H, int Nk_max, int dk, int dv, int chunk,
+                    int dtype, float scale, const void* workspace,
+                    size_t workspace_bytes);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_str(int status);
+
+/* Version of this ABI (major * 100 + minor). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONLINE_SOFTMAX_FA_H */

@@ -1,0 +1,223 @@
+"""Thin Python binding of libfa.so (exact attention forward on MI355X).
+
+Argument marshalling only: the functions below check dtypes, shapes,
+contiguity and device, allocate outputs with torch, and pass raw device
+pointers and torch's current HIP stream to the C ABI (include/fa.h).  Every
+step of the computation runs in the library's HIP kernels; there is no CPU
+or PyTorch fallback.  If libfa.so is missing, every call raises.
+
+The names match the C entry points: fa_fwd, fa_decode_splitk,
+fa_decode_splitk_workspace_bytes, fa_check_fwd, fa_check_decode,
+fa_status_str, fa_abi_version.
+"""
+
+import ctypes
+import math
+import os
+import pathlib
+
+# torch must own the process's HIP runtime before libfa.so is loaded, so that
+# the library binds to the very same runtime (both carry the soname
+# libamdhip64.so.7) and pointers and streams mean the same thing on both sides.
+import torch
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FaError", "lib", "lib_path",
+    "fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
+    "fa_check_fwd", "fa_check_decode", "fa_status_str", "fa_abi_version",
+]
+
+FA_F32 = 0
+FA_BF16 = 1
+_STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+           4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
+
+_LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
+_lib = None
+
+_vp, _fp, _ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_i, _f, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_check_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i]),
+    "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
+    "fa_status_str": (ctypes.c_char_p, [_i]),
+    "fa_abi_version": (_i, []),
+}
+
+
+class FaError(RuntimeError):
+    """A nonzero fa_status from the library, or a binding-level misuse."""
+
+    def __init__(self, status, msg=None):
+        self.status = status
+        super().__init__(msg or f"{_STATUS.get(status, status)}: {fa_status_str(status)}")
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+
+
+def lib():
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not _LIB_PATH.exists():
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m online_softmax_05_amd.build`")
+        handle = ctypes.CDLL(str(_LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        runtimes = _hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise RuntimeError(f"two HIP runtimes are mapped in this process: {sorted(runtimes)}")
+        _lib = handle
+    return _lib
+
+
+def fa_status_str(status):
+    return lib().fa_status_str(int(status)).decode()
+
+
+def fa_abi_version():
+    return lib().fa_abi_version()
+
+
+def fa_decode_splitk_workspace_bytes(B, H, Nk_max, dv, chunk=512):
+    return lib().fa_decode_splitk_workspace_bytes(B, H, Nk_max, dv, chunk)
+
+
+def fa_check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n):
+    """Host-only validation; pointers are plain integers (or None)."""
+    return lib().fa_check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale,
+                              int(causal), block_n)
+
+
+def fa_check_decode(q, k, v, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, workspace,
+                    workspace_bytes):
+    return lib().fa_check_decode(q, k, v, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale,
+                                 workspace, workspace_bytes)
+
+
+# --------------------------------------------------------------------------
+# torch-facing calls
+# --------------------------------------------------------------------------
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise FaError(3, f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, dims=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise FaError(1, f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise FaError(3, f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise FaError(3, f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise FaError(2, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise FaError(3, f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise FaError(2, f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fa_fwd(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, block_n=0, out=None, lse=None,
+           want_lse=True):
+    """Attention forward: q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv] (bf16 or fp32),
+    bias fp32 [B,H,Nq,Nk] or None, k_len int32 [B] or None.  Returns (o, lse)."""
+    _need(q, "q", dims=4)
+    dev = q.device
+    _need(k, "k", dtype=q.dtype, dims=4, device=dev)
+    _need(v, "v", dtype=q.dtype, dims=4, device=dev)
+    B, H, Nq, dk = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, Nk, dk) or tuple(v.shape) != (B, H, Nk, dv):
+        raise FaError(2, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if bias is not None:
+        _need(bias, "bias", dtype=torch.float32, dims=4, device=dev)
+        if tuple(bias.shape) != (B, H, Nq, Nk):
+            raise FaError(2, f"bias must be {(B, H, Nq, Nk)}, got {tuple(bias.shape)}")
+    if k_len is not None:
+        _need(k_len, "k_len", dtype=torch.int32, dims=1, device=dev)
+        if k_len.shape[0] != B:
+            raise FaError(2, f"k_len must have {B} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=dev)
+    else:
+        _need(out, "out", dtype=q.dtype, dims=4, device=dev)
+        if tuple(out.shape) != (B, H, Nq, dv):
+            raise FaError(2, "out has the wrong shape")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need(lse, "lse", dtype=torch.float32, dims=3, device=dev)
+        if tuple(lse.shape) != (B, H, Nq):
+            raise FaError(2, "lse has the wrong shape")
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(k_len), _ptr(out), _ptr(lse),
+                      B, H, Nq, Nk, dk, dv, _dtype_code(q), float(scale), int(bool(causal)), int(block_n),
+                      _stream(dev))
+    if st != 0:
+        raise FaError(st)
+    return out, lse
+
+
+def fa_decode_splitk(q, k_cache, v_cache, k_len, *, scale=None, chunk=512, out=None, lse=None,
+                     workspace=None, want_lse=True):
+    """Single-token decode: q [B,H,dk], caches [B,H,Nk_max,d], k_len int32 [B]
+    (required).  The fp32 workspace is allocated with torch unless given.
+    Returns (o [B,H,dv], lse [B,H])."""
+    _need(q, "q", dims=3)
+    dev = q.device
+    _need(k_cache, "k_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(v_cache, "v_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(k_len, "k_len", dtype=torch.int32, dims=1, device=dev)
+    B, H, dk = q.shape
+    Nk, dv = k_cache.shape[2], v_cache.shape[3]
+    if tuple(k_cache.shape) != (B, H, Nk, dk) or tuple(v_cache.shape) != (B, H, Nk, dv):
+        raise FaError(2, "cache shapes do not match q")
+    if k_len.shape[0] != B:
+        raise FaError(2, f"k_len must have {B} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    need = fa_decode_splitk_workspace_bytes(B, H, Nk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    else:
+        _need(workspace, "workspace", dtype=torch.float32, dims=1, device=dev)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib().fa_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_len), _ptr(out), _ptr(lse),
+                                B, H, Nk, dk, dv, int(chunk), _dtype_code(q), float(scale),
+                                _ptr(workspace), workspace.numel() * 4, _stream(dev))
+    if st != 0:
+        raise FaError(st)
+    return out, lse

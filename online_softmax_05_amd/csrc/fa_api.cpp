@@ -1,0 +1,145 @@
+// Host front end of libfa.so: argument validation and kernel dispatch for
+// the C ABI declared in include/fa.h.  Validation never dereferences a
+// pointer and never touches the GPU, so the fa_check_* entry points run on
+// machines without one.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxHeadDim = 128;
+constexpr int kMaxChunk = 2048;
+constexpr long long kInt32Max = std::numeric_limits<int32_t>::max();
+
+bool product_fits(std::initializer_list<long long> xs, long long limit) {
+  long long p = 1;
+  for (long long x : xs) {
+    if (x < 0) return false;
+    if (x != 0 && p > limit / x) return false;
+    p *= x;
+  }
+  return p <= limit;
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+              const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
+              float scale, int causal, int block_n) {
+  (void)bias;
+  (void)k_len;
+  (void)lse;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (dk < 1 || dv < 1) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dk > kMaxHeadDim || dv > kMaxHeadDim) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (block_n != 0 && block_n != 32 && block_n != 64 && block_n != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  // element offsets are formed in 64 bits; grid sizes and per-(b,h) row
+  // counts must fit the 32-bit launch and index arithmetic
+  const long long n_qt = (Nq + 127LL) / 128;
+  if (!product_fits({n_qt, H, B}, kInt32Max)) return FA_ERR_SHAPE;
+  if (!product_fits({B, H}, kInt32Max)) return FA_ERR_SHAPE;
+  if (Nq > kInt32Max - Nk) return FA_ERR_SHAPE;
+  if ((long long)B * H * Nq == 0) return FA_OK;  // nothing to compute
+  if (q == nullptr || o == nullptr) return FA_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
+  return FA_OK;
+}
+
+int check_decode(const void* q, const void* k, const void* v, const int32_t* k_len, const void* o,
+                 const float* lse, int B, int H, int Nk, int dk, int dv, int chunk, int dtype, float scale,
+                 const void* workspace, size_t workspace_bytes) {
+  (void)lse;
+  if (B < 0 || H < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (dk < 1 || dv < 1) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dk > kMaxHeadDim || dv > kMaxHeadDim) return FA_ERR_UNSUPPORTED;
+  if (chunk < 64 || chunk > kMaxChunk || chunk % 64 != 0) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  const long long max_chunks = (Nk + (long long)chunk - 1) / chunk;
+  if (!product_fits({B, H, std::max(max_chunks, 1LL)}, kInt32Max)) return FA_ERR_SHAPE;
+  if ((long long)B * H == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || k_len == nullptr) return FA_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
+  const size_t need = fa_decode_splitk_workspace_bytes(B, H, Nk, dv, chunk);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return FA_ERR_WORKSPACE;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 100; }
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or too large shape";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block_n, chunk, causal flag or scale";
+    case FA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_check_fwd(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+                 const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
+                 float scale, int causal, int block_n) {
+  return check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len, void* o,
+           float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype, float scale, int causal,
+           int block_n, void* stream) {
+  const int st = check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal, block_n == 0 ? 64 : block_n};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, static_cast<hipStream_t>(stream))
+                                        : fa::launch_fwd_f32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_splitk_workspace_bytes(int B, int H, int Nk_max, int dv, int chunk) {
+  if (B < 0 || H < 0 || Nk_max < 0 || dv < 1 || chunk < 64 || chunk % 64 != 0) return 0;
+  const size_t max_chunks = ((size_t)Nk_max + chunk - 1) / chunk;
+  return (size_t)B * H * max_chunks * ((size_t)dv + 2) * sizeof(float);
+}
+
+int fa_check_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* k_len, const void* o,
+                    const float* lse, int B, int H, int Nk_max, int dk, int dv, int chunk, int dtype, float scale,
+                    const void* workspace, size_t workspace_bytes) {
+  return check_decode(q, k_cache, v_cache, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, workspace,
+                      workspace_bytes);
+}
+
+int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int32_t* k_len, void* o,
+                     float* lse, int B, int H, int Nk_max, int dk, int dv, int chunk, int dtype, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_decode(q, k_cache, v_cache, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale,
+                              workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0) return FA_OK;
+  const int max_chunks = (int)(((long long)Nk_max + chunk - 1) / chunk);
+  float* ws = static_cast<float*>(workspace);
+  fa::DecodeArgs a{q, k_cache, v_cache, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, scale,
+                   ws, ws == nullptr ? nullptr : ws + (size_t)B * H * max_chunks * dv, max_chunks};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_decode_bf16(a, static_cast<hipStream_t>(stream))
+                                        : fa::launch_decode_f32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

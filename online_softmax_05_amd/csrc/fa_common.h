@@ -1,0 +1,107 @@
+// Device-side helpers shared by the attention kernels (gfx950 only).
+//
+// Sources, cited by title and section:
+//   [GS] "How Does FlashAttention Preserve Global Softmax Across Tiles?"
+//   [VW] "Flash attention and efficient attention: Visual walkthrough"
+//   [OA] "Reducing Memory Traffic with Output Accumulation in FlashAttention"
+//
+// All softmax arithmetic runs in the base-2 domain: a logit s is carried as
+// t = s * log2(e), so exp(s - m) = exp2(t - m2) maps onto the hardware
+// v_exp_f32, and lse = ln(2) * (m2 + log2(l)).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  // v_exp_f32; exp2(-inf) = 0, which is how masked logits drop out
+  // ([VW] Step 7: a masked score contributes nothing).
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by the lane 32 positions away (lane ^ 32), combined with `op`:
+// v_permlane32_swap returns {[lo, lo], [hi, hi]} for an input [lo, hi].
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// bf16 <-> f32 (round to nearest even on the way down: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Work-group -> (batch*head, query tile) mapping.
+//
+// Work-groups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
+// its own L2.  Renumbering so that XCD x works through a contiguous range of
+// logical tiles keeps the query tiles of one (batch, head) -- which re-read
+// the same K/V -- on one L2.  Inside a (batch, head) the tiles are issued
+// heaviest first when a causal mask makes later query tiles longer.
+struct TileCoord {
+  int bh;
+  int qt;
+};
+__device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool heavy_first) {
+  int lid = pid;
+  if ((total & 7) == 0) lid = (pid & 7) * (total >> 3) + (pid >> 3);
+  TileCoord c;
+  c.bh = lid / n_qt;
+  int r = lid - c.bh * n_qt;
+  c.qt = heavy_first ? (n_qt - 1 - r) : r;
+  return c;
+}
+
+// Number of keys a row block must visit: keys at or past `n_end` are masked
+// for every row of the block, so whole tiles past it are skipped ([GS]
+// section 6: entirely masked tiles can be skipped).  `last_row` is the last
+// query row of the block (global index).
+__device__ __forceinline__ int visible_key_end(int klen_eff, bool causal, int last_row, int nq, int nk) {
+  int end = klen_eff;
+  if (causal) {
+    long long c = (long long)last_row + nk - nq + 1;  // bottom-right diagonal
+    if (c < end) end = (int)(c < 0 ? 0 : c);
+  }
+  return end;
+}
+
+// Four consecutive fp32 bias values of one row starting at key0, zero past
+// nk or for an invalid row; vec: the row is 16-byte aligned and nk % 4 == 0.
+__device__ __forceinline__ f32x4 load_bias4(const float* brow, int key0, int nk, bool vec, bool valid) {
+  f32x4 w = {0.f, 0.f, 0.f, 0.f};
+  if (!valid) return w;
+  if (vec && key0 + 3 < nk) return *reinterpret_cast<const f32x4*>(brow + key0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (key0 + j < nk) ? brow[key0 + j] : 0.f;
+  return w;
+}
+
+__device__ __forceinline__ int clamp_klen(const int32_t* k_len, int b, int nk) {
+  if (k_len == nullptr) return nk;
+  int x = k_len[b];
+  return x < 0 ? 0 : (x > nk ? nk : x);
+}
+
+}  // namespace fa

@@ -1,0 +1,246 @@
+// Single-token decode against a KV cache, split over key chunks.
+//
+// Sources, cited by title and section:
+//   [GS] "How Does FlashAttention Preserve Global Softmax Across Tiles?"
+//   [VW] "Flash attention and efficient attention: Visual walkthrough"
+//
+// With one query row there is nothing to reuse: every cached key and value
+// is read once, so the pass is bound by HBM bandwidth ([GS] section 8, the
+// single-token decode case).  To spread one row's keys over the whole chip
+// the key axis is split into chunks ([GS] section 8, split KV loading for
+// short queries):
+//
+//   partial kernel  one work-group per (batch, head, chunk) that holds at
+//                   least one allowed key.  It computes the chunk's own state
+//                   (m_c, l_c, u_c) by its definition ([VW] Step 4): pass 1
+//                   streams K and writes the chunk's logits to LDS, the chunk
+//                   maximum is reduced, pass 2 streams V and accumulates
+//                   u_c = sum exp(t - m_c) v.  Inside a chunk the maximum is
+//                   known before any exponential is taken, so no rescaling is
+//                   needed there.
+//   merge kernel    one wave per (batch, head): rebases every chunk state to
+//                   the common maximum and sums, in ascending chunk order
+//                   ([GS] section 4; [VW] Step 5), then divides once.  A
+//                   sequence with no key gets o = 0, lse = -inf ([GS]
+//                   section 6).
+//
+// Logits are carried in the base-2 domain (t = s * log2 e), so m_c is a
+// base-2 maximum and lse = ln2 * (m + log2 l).
+#include "fa_common.h"
+#include "launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxChunk = 2048;  // LDS logit buffer (8 KiB)
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {
+  static constexpr int VEC = 8;  // elements per 16-byte load
+  __device__ static void load(const uint16_t* row, int d0, int d, bool vec, float* out) {
+    if (vec) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (d0 < d) w = *reinterpret_cast<const u32x4*>(row + d0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        out[2 * p] = bf16_lo(w[p]);
+        out[2 * p + 1] = bf16_hi(w[p]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = (d0 + e < d) ? bf16_to_f32(row[d0 + e]) : 0.f;
+    }
+  }
+  __device__ static uint16_t store(float x) { return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int VEC = 4;
+  __device__ static void load(const float* row, int d0, int d, bool vec, float* out) {
+    if (vec) {
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+      if (d0 < d) w = *reinterpret_cast<const f32x4*>(row + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = w[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (d0 + e < d) ? row[d0 + e] : 0.f;
+    }
+  }
+  __device__ static float store(float x) { return x; }
+};
+
+// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane
+// of a group ends with the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename T, int DKP, int DVP>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ k_len,
+    float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int Nk, int dk, int dv, int chunk, int max_chunks,
+    float scale_log2, int vec_k, int vec_v) {
+  using E = Elem<T>;
+  constexpr int VEC = E::VEC;
+  constexpr int LPK = DKP / VEC;  // lanes per K row
+  constexpr int RPK = 64 / LPK;   // K rows per wave load
+  constexpr int LPV = DVP / VEC;
+  constexpr int RPV = 64 / LPV;
+  __shared__ float sc[kMaxChunk];
+  __shared__ float red[4][DVP];
+  __shared__ float stat[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bhi = blockIdx.x / max_chunks;
+  const int c = blockIdx.x - bhi * max_chunks;
+  const int b = bhi / H;
+  const int klen = clamp_klen(k_len, b, Nk);
+  const int c0 = c * chunk;
+  if (c0 >= klen) return;  // no allowed key in this chunk: no state
+  const int len = min(chunk, klen - c0);
+
+  const size_t bh = (size_t)bhi;
+  const T* kbh = k + bh * Nk * dk;
+  const T* vbh = v + bh * Nk * dv;
+
+  // ---- pass 1: logits of the chunk (base 2) ------------------------------
+  float qf[VEC];
+  E::load(q + bh * dk, (lane % LPK) * VEC, dk, vec_k != 0, qf);
+  const int n_groups_k = (len + RPK - 1) / RPK;
+#pragma unroll 4
+  for (int g = wave; g < n_groups_k; g += 4) {
+    const int r = g * RPK + lane / LPK;  // row within the chunk
+    float kf[VEC];
+    if (r < len) {
+      E::load(kbh + (size_t)(c0 + r) * dk, (lane % LPK) * VEC, dk, vec_k != 0, kf);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) kf[e] = 0.f;
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot = fmaf(qf[e], kf[e], dot);
+    dot = group_sum<LPK>(dot);
+    if ((lane % LPK) == 0 && r < len) sc[r] = dot * scale_log2;
+  }
+  __syncthreads();
+
+  // ---- chunk maximum and denominator ----------------------------------
+  float mx = kNegInf;
+  for (int j = tid; j < len; j += kThreads) mx = fmaxf(mx, sc[j]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) stat[wave] = mx;
+  __syncthreads();
+  const float m_c = fmaxf(fmaxf(stat[0], stat[1]), fmaxf(stat[2], stat[3]));
+  float ls = 0.f;
+  for (int j = tid; j < len; j += kThreads) ls += fast_exp2(sc[j] - m_c);
+  ls = group_sum<64>(ls);
+  if (lane == 0) stat[4 + wave] = ls;
+
+  // ---- pass 2: u_c = sum_j exp2(t_j - m_c) v_j ----------------------------
+  float u[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) u[e] = 0.f;
+  const int n_groups_v = (len + RPV - 1) / RPV;
+#pragma unroll 4
+  for (int g = wave; g < n_groups_v; g += 4) {
+    const int r = g * RPV + lane / LPV;
+    if (r < len) {
+      float vf[VEC];
+      E::load(vbh + (size_t)(c0 + r) * dv, (lane % LPV) * VEC, dv, vec_v != 0, vf);
+      const float p = fast_exp2(sc[r] - m_c);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) u[e] = fmaf(p, vf[e], u[e]);
+    }
+  }
+  // lanes holding the same dims: reduce across the rows of a wave
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+#pragma unroll
+    for (int off = LPV; off < 64; off <<= 1) u[e] += __shfl_xor(u[e], off);
+  }
+  if (lane < LPV) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red[wave][lane * VEC + e] = u[e];
+  }
+  __syncthreads();
+  float* wu = ws_u + (bh * max_chunks + c) * (size_t)dv;
+  for (int d = tid; d < dv; d += kThreads) wu[d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
+  if (tid == 0) {
+    float* wml = ws_ml + (bh * max_chunks + c) * 2;
+    wml[0] = m_c;
+    wml[1] = stat[4] + stat[5] + stat[6] + stat[7];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ ws_u,
+                                                          const float* __restrict__ ws_ml,
+                                                          const int32_t* __restrict__ k_len, T* __restrict__ o,
+                                                          float* __restrict__ lse, int H, int Nk, int dv, int chunk,
+                                                          int max_chunks) {
+  const int bhi = blockIdx.x;
+  const int b = bhi / H;
+  const int lane = threadIdx.x;
+  const int klen = clamp_klen(k_len, b, Nk);
+  const int n_c = (klen + chunk - 1) / chunk;
+  const size_t base = (size_t)bhi * max_chunks;
+  float m = kNegInf;
+  for (int c = 0; c < n_c; ++c) m = fmaxf(m, ws_ml[(base + c) * 2]);
+  float l = 0.f;
+  for (int c = 0; c < n_c; ++c) l = fmaf(fast_exp2(ws_ml[(base + c) * 2] - m), ws_ml[(base + c) * 2 + 1], l);
+  const bool nonempty = n_c > 0 && l > 0.f;
+  const float inv = nonempty ? 1.f / l : 0.f;
+  T* orow = o + (size_t)bhi * dv;
+  for (int d = lane; d < dv; d += 64) {
+    float u = 0.f;
+    for (int c = 0; c < n_c; ++c) u = fmaf(fast_exp2(ws_ml[(base + c) * 2] - m), ws_u[(base + c) * dv + d], u);
+    orow[d] = Elem<T>::store(u * inv);
+  }
+  if (lse != nullptr && lane == 0) lse[bhi] = nonempty ? (m + fast_log2(l)) * kLn2 : kNegInf;
+}
+
+template <typename T, int DKP, int DVP>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const int vec = Elem<T>::VEC;
+  const uintptr_t m16 = 15;
+  const bool vec_k = (a.dk % vec == 0) && (((uintptr_t)a.k & m16) == 0) && (((uintptr_t)a.q & m16) == 0);
+  const bool vec_v = (a.dv % vec == 0) && (((uintptr_t)a.v & m16) == 0);
+  const long long n_part = (long long)a.B * a.H * a.max_chunks;
+  if (n_part > 0) {
+    hipLaunchKernelGGL((decode_partial_kernel<T, DKP, DVP>), dim3((unsigned)n_part), dim3(kThreads), 0, stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.k_len, a.ws_u, a.ws_ml, a.H, a.Nk, a.dk, a.dv,
+                       a.chunk, a.max_chunks, a.scale * kLog2e, (int)vec_k, (int)vec_v);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<T>), dim3((unsigned)(a.B * a.H)), dim3(64), 0, stream, a.ws_u, a.ws_ml,
+                     a.k_len, (T*)a.o, a.lse, a.H, a.Nk, a.dv, a.chunk, a.max_chunks);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  const bool k64 = a.dk <= 64, v64 = a.dv <= 64;
+  if (k64 && v64) return launch_t<T, 64, 64>(a, s);
+  if (k64) return launch_t<T, 64, 128>(a, s);
+  if (v64) return launch_t<T, 128, 64>(a, s);
+  return launch_t<T, 128, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) { return launch_d<uint16_t>(a, s); }
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_d<float>(a, s); }
+
+}  // namespace fa

@@ -1,0 +1,44 @@
+// Internal launcher interface between the C-ABI front end (fa_api.cpp) and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* bias;
+  const int32_t* k_len;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk, dk, dv;
+  float scale;
+  int causal;
+  int block_n;  // 32, 64 or 128 (already resolved from "auto")
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* k_len;
+  void* o;
+  float* lse;
+  int B, H, Nk, dk, dv, chunk;
+  float scale;
+  float* ws_u;   // [B*H*max_chunks, dv]
+  float* ws_ml;  // [B*H*max_chunks, 2]  (m in the base-2 domain, l)
+  int max_chunks;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,378 @@
+"""GPU parity: the HIP library (through the C ABI binding) against the float64
+oracle, element by element, on the same seeded inputs.
+
+Tolerances (max abs over all compared elements): fp32 inputs 1e-5 for o and
+lse; bf16 inputs 2e-2 for o and 1e-3 for lse; empty rows exactly o = 0 and
+lse = -inf.  Small workloads are compared in full; the full-size prefill,
+long-context and decode workloads -- in the launch configuration the
+benchmark times -- are compared on sampled rows that the oracle computes one
+by one, plus properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pins
+from tests.parity_util import TOL, compare, f64, oracle_full, oracle_rows, say, scale32
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_05_amd as fa
+
+    fa.lib()
+    return torch.device("cuda:0")
+
+
+def run_fwd(inp, dev, block_n=None):
+    import online_softmax_05_amd as fa
+
+    d = workloads.to_device(inp, dev)
+    o, lse = fa.fa_fwd(d["q"], d["k"], d["v"], bias=d.get("bias"), k_len=d.get("k_len"), scale=inp["scale"],
+                       causal=inp["causal"], block_n=inp.get("block_n", 0) if block_n is None else block_n)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples, through the GPU
+# ---------------------------------------------------------------------------
+
+GOLDEN_CASES = ["gs_sec2_tile_local_counterexample.json", "gs_sec4_rescale_both.json", "vw_step6_row0.json",
+                "oa_fig1_weighted_sum_first.json", "oa_fig2_chunk_states.json", "oa_fig3_two_queries.json"]
+
+
+@pytest.mark.parametrize("name", GOLDEN_CASES)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_worked_examples(dev, name, dt):
+    fx = pins.load_golden(name)
+    dtype = DT[dt]
+    q = torch.tensor(fx["q"], dtype=torch.float32)[None, None].to(dtype)
+    k = torch.tensor(fx["k"], dtype=torch.float32)[None, None].to(dtype)
+    v = torch.tensor(fx["v"], dtype=torch.float32)[None, None].to(dtype)
+    inp = dict(q=q, k=k, v=v, bias=None, k_len=None, causal=False, scale=float(fx["scale"]))
+    say(f"worked example {name} {dt}")
+    for bn in (32, 64, 128):
+        o, lse = run_fwd(inp, dev, block_n=bn)
+        o_ref, lse_ref = oracle_full(inp)
+        compare(o, lse, o_ref, lse_ref, dtype, f"{name} {dt} block_n={bn}")
+    if dt == "f32":
+        # the page's printed output, at the printed precision
+        want = np.asarray(fx["expected"]["o"], dtype=np.float64).reshape(o_ref.shape[2:])
+        assert np.max(np.abs(f64(o)[0, 0] - want)) <= fx["tolerance"] + 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the pages' CPU-check shape families, run on the GPU
+# ---------------------------------------------------------------------------
+
+FAMILY_CASES = [
+    # (Nq, Nk, dk, dv, causal, k_len)
+    (5, 9, 4, 3, False, None),
+    (7, 7, 5, 2, True, None),
+    (2, 6, 1, 1, True, None),
+    (5, 2, 1, 1, True, None),     # Nq > Nk: rows 0-2 empty
+    (2, 4, 3, 2, True, [1]),
+    (4, 7, 3, 4, True, [0]),      # padded-away sequence: every row empty
+    (4, 7, 3, 4, False, [5]),
+    (2, 0, 3, 2, False, None),    # empty key axis
+    (1, 5, 1, 1, False, None),
+    (1, 5, 1, 2, False, None),
+    (3, 6, 4, 3, False, None),
+]
+
+
+@pytest.mark.parametrize("case", FAMILY_CASES, ids=lambda c: "x".join(map(str, c[:4])) + ("c" if c[4] else ""))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_page_families(dev, case, dt):
+    nq, nk, dk, dv, causal, k_len = case
+    inp = workloads.seeded_case(1000 + nq * 100 + nk, 1, 1, nq, nk, dk, dv, DT[dt], causal=causal,
+                                bias=False, k_len=k_len)
+    say(f"family {case} {dt}")
+    o, lse = run_fwd(inp, dev)
+    o_ref, lse_ref = oracle_full(inp)
+    compare(o, lse, o_ref, lse_ref, DT[dt], f"family {case} {dt}")
+
+
+def test_wide_logit_span(dev):
+    """Large common shifts and a wide span of finite logits, through the bias."""
+    bias = torch.tensor([0.0, 40.0, -40.0, 39.5, 1.0], dtype=torch.float32).repeat(3, 1)
+    bias[1] += 1000.0
+    bias[2] -= 2000.0
+    for dt in ("f32", "bf16"):
+        inp = workloads.seeded_case(77, 1, 1, 3, 5, 2, 2, DT[dt])
+        inp["bias"] = bias[None, None].clone()
+        say(f"wide logit span {dt}")
+        o, lse = run_fwd(inp, dev)
+        o_ref, lse_ref = oracle_full(inp)
+        tol_lse = 1e-5 if dt == "f32" else 1e-3
+        # lse is ~2000 in magnitude here: compare it relative to its size
+        assert np.max(np.abs(f64(lse) - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= tol_lse
+        assert np.max(np.abs(f64(o) - o_ref)) <= TOL[DT[dt]]["o"]
+
+
+# ---------------------------------------------------------------------------
+# the small and masks workloads, compared in full
+# ---------------------------------------------------------------------------
+
+def test_small_workload_all_tiles(dev):
+    inp = workloads.small()
+    o_ref, lse_ref = oracle_full(inp)
+    outs = []
+    for bn in (64, 32, 128):
+        say(f"small workload fp32 block_n={bn}")
+        o, lse = run_fwd(inp, dev, block_n=bn)
+        compare(o, lse, o_ref, lse_ref, torch.float32, f"small block_n={bn}")
+        outs.append((f64(o), f64(lse)))
+    # tile-size invariance beyond the oracle check
+    for o, lse in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 2e-6
+        assert np.max(np.abs(lse - outs[0][1])) <= 2e-6
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_masks_workload(dev, dt):
+    inp = workloads.masks(DT[dt])
+    say(f"masks workload {dt}, k_len={inp['k_len'].tolist()}")
+    o_ref, lse_ref = oracle_full(inp)
+    assert np.all(np.isneginf(lse_ref[0])), "sequence 0 (k_len = 0) must be all empty rows"
+    for bn in (0, 32, 128):
+        o, lse = run_fwd(inp, dev, block_n=bn)
+        compare(o, lse, o_ref, lse_ref, DT[dt], f"masks {dt} block_n={bn}")
+    # equal-logit rows: the plain mean of the visible values ([VW] Step 7)
+    v = f64(inp["v"])
+    klen = inp["k_len"].tolist()
+    nq = nk = workloads.SHAPES["masks"]["Nq"]
+    og = f64(o)
+    for b in range(2):
+        for i in inp["equal_rows"].tolist():
+            cnt = min(klen[b], i + nk - nq + 1)
+            for h in range(4):
+                if cnt <= 0:
+                    assert np.all(og[b, h, i] == 0.0)
+                else:
+                    mean = v[b, h, :cnt].mean(axis=0)
+                    assert np.max(np.abs(og[b, h, i] - mean)) <= TOL[DT[dt]]["o"]
+
+
+# ---------------------------------------------------------------------------
+# seeded sweep over ragged shapes, head dims, masks and dtypes
+# ---------------------------------------------------------------------------
+
+def _sweep_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    dims = [(128, 128), (64, 64), (128, 64), (64, 128), (32, 32), (8, 16), (100, 72), (1, 1), (3, 5), (96, 128)]
+    for n in range(30):
+        dk, dv = dims[n % len(dims)]
+        nq = int(rng.choice([1, 7, 31, 32, 33, 127, 128, 129, 200, 300, 513]))
+        nk = int(rng.choice([0, 1, 5, 63, 64, 65, 130, 257, 400, 700]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        causal = bool(rng.integers(0, 2))
+        bias = bool(rng.integers(0, 2))
+        kl = [None, "random"][int(rng.integers(0, 2))]
+        dt = ["f32", "bf16"][n % 2]
+        bn = [0, 32, 64, 128][int(rng.integers(0, 4))]
+        cases.append((n, B, H, nq, nk, dk, dv, dt, causal, bias, kl, bn))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"s{c[0]}")
+def test_seeded_sweep(dev, case):
+    n, B, H, nq, nk, dk, dv, dt, causal, bias, kl, bn = case
+    inp = workloads.seeded_case(5000 + n, B, H, nq, nk, dk, dv, DT[dt], causal=causal, bias=bias, k_len=kl)
+    say(f"sweep {case} k_len={None if inp['k_len'] is None else inp['k_len'].tolist()}")
+    o, lse = run_fwd(inp, dev, block_n=bn)
+    o_ref, lse_ref = oracle_full(inp)
+    compare(o, lse, o_ref, lse_ref, DT[dt], f"sweep {n}")
+
+
+def test_k_len_clamped(dev):
+    """k_len outside [0, Nk] is clamped by the kernels."""
+    inp = workloads.seeded_case(31, 3, 2, 40, 50, 64, 64, torch.bfloat16, causal=False, k_len=[-5, 77, 20])
+    say("k_len clamp")
+    o, lse = run_fwd(inp, dev)
+    ref = dict(inp)
+    ref["k_len"] = torch.tensor([0, 50, 20], dtype=torch.int32)
+    o_ref, lse_ref = oracle_full(ref)
+    compare(o, lse, o_ref, lse_ref, torch.bfloat16, "k_len clamp")
+
+
+def test_run_to_run_bitwise(dev):
+    inp = workloads.seeded_case(4242, 2, 3, 300, 333, 128, 128, torch.bfloat16, causal=True, bias=True,
+                                k_len="random")
+    say("determinism")
+    o1, l1 = run_fwd(inp, dev)
+    o2, l2 = run_fwd(inp, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_optional_and_out_reuse(dev):
+    import online_softmax_05_amd as fa
+
+    inp = workloads.seeded_case(99, 1, 2, 65, 70, 64, 64, torch.float32, causal=True)
+    d = workloads.to_device(inp, dev)
+    say("lse optional")
+    o1, _ = fa.fa_fwd(d["q"], d["k"], d["v"], causal=True, want_lse=False)
+    out = torch.full_like(o1, float("nan"))
+    o2, l2 = fa.fa_fwd(d["q"], d["k"], d["v"], causal=True, out=out)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == out.data_ptr()
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# full-size prefill and long-context workloads (sampled rows)
+# ---------------------------------------------------------------------------
+
+def _sample_rows(rng, B, H, N, n_random, tile=128):
+    rows = set()
+    special = [0, 1, 31, 32, 63, 64, tile - 1, tile, tile + 1, N // 2 - 1, N // 2, N - tile - 1, N - tile,
+               N - 2, N - 1]
+    for _ in range(n_random):
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, N))))
+    for i in special:
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, H)), i))
+    rows.add((B - 1, H - 1, N - 1))
+    rows.add((0, 0, 0))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["prefill", "long"])
+def test_full_size_sampled(dev, name):
+    import online_softmax_05_amd as fa
+
+    say(f"{name}: drawing inputs on the device")
+    inp = getattr(workloads, name)(dev)
+    say(f"{name}: fa_fwd (the benchmark's launch configuration)")
+    o, lse = fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"])
+    torch.cuda.synchronize()
+    s = workloads.SHAPES[name]
+    B, H, N = s["B"], s["H"], s["Nq"]
+    rng = np.random.default_rng(7 if name == "prefill" else 8)
+    rows = _sample_rows(rng, B, H, N, 96 if name == "prefill" else 48)
+    say(f"{name}: oracle on {len(rows)} sampled rows")
+    o_ref, lse_ref = oracle_rows(inp["q"], inp["k"], inp["v"], rows, scale=inp["scale"], causal=True)
+    og = np.stack([f64(o[b, h, i]) for b, h, i in rows])
+    lg = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    compare(torch.from_numpy(og), torch.from_numpy(lg), o_ref, lse_ref, torch.bfloat16, f"{name} sampled rows")
+    # properties over every row: finite, and lse >= its own row's first logit
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # row 0 sees exactly key 0 (bottom-right causal, Nq == Nk): o = v_0, lse = s_00
+    v0 = inp["v"][:, :, 0, :].float()
+    assert torch.max(torch.abs(o[:, :, 0, :].float() - v0)).item() <= 1e-2
+    s00 = (inp["q"][:, :, 0, :].float() * inp["k"][:, :, 0, :].float()).sum(-1) * scale32(inp["scale"])
+    assert torch.max(torch.abs(lse[:, :, 0] - s00)).item() <= 1e-3
+    del inp, o, lse
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# split-K decode
+# ---------------------------------------------------------------------------
+
+def _decode_oracle(q, k, v, k_len_host, pairs, scale):
+    o = np.zeros((len(pairs), v.shape[3]))
+    lse = np.zeros(len(pairs))
+    for n, (b, h) in enumerate(pairs):
+        kl = int(k_len_host[b])
+        ob, lb = oracle.attention_head(f64(q[b, h][None]), f64(k[b, h, :kl]), f64(v[b, h, :kl]),
+                                       scale=scale32(scale), nq=1, causal=False)
+        o[n], lse[n] = ob[0], lb[0]
+    return o, lse
+
+
+def test_decode_full_size_sampled(dev):
+    import online_softmax_05_amd as fa
+
+    say("decode: drawing inputs on the device")
+    inp = workloads.decode(dev)
+    say("decode: fa_decode_splitk (the benchmark's launch configuration)")
+    o, lse = fa.fa_decode_splitk(inp["q"], inp["k"], inp["v"], inp["k_len"], scale=inp["scale"],
+                                 chunk=inp["chunk"])
+    torch.cuda.synchronize()
+    kl = inp["k_len_host"]
+    rng = np.random.default_rng(55)
+    B, H = workloads.SHAPES["decode"]["B"], workloads.SHAPES["decode"]["H"]
+    pairs = sorted({(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(48)}
+                   | {(int(np.argmin(kl)), 0), (int(np.argmax(kl)), H - 1)})
+    say(f"decode: oracle on {len(pairs)} sampled (b, h)")
+    o_ref, lse_ref = _decode_oracle(inp["q"], inp["k"], inp["v"], kl, pairs, inp["scale"])
+    og = np.stack([f64(o[b, h]) for b, h in pairs])
+    lg = np.array([float(lse[b, h]) for b, h in pairs])
+    compare(torch.from_numpy(og), torch.from_numpy(lg), o_ref, lse_ref, torch.bfloat16, "decode sampled")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    del inp, o, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 512, 2048])
+def test_decode_small_full(dev, dt, chunk):
+    import online_softmax_05_amd as fa
+
+    g = torch.Generator().manual_seed(chunk)
+    B, H, Nk, dk, dv = 5, 3, 1500, 128, 64
+    q = torch.randn(B, H, dk, generator=g).to(DT[dt])
+    k = torch.randn(B, H, Nk, dk, generator=g).to(DT[dt])
+    v = torch.randn(B, H, Nk, dv, generator=g).to(DT[dt])
+    k_len = torch.tensor([0, 1, 700, 1500, 9999], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(dk)
+    say(f"decode small {dt} chunk={chunk}")
+    o, lse = fa.fa_decode_splitk(q.to(dev), k.to(dev), v.to(dev), k_len.to(dev), scale=scale, chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(f64(q)[:, :, None], f64(k), f64(v), scale=scale32(scale),
+                                          k_len=np.clip(k_len.numpy(), 0, Nk))
+    compare(o[:, :, None], lse[:, :, None], o_ref, lse_ref, DT[dt], f"decode {dt} chunk={chunk}")
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (40, 24), (1, 1)])
+def test_decode_matches_fwd_nq1(dev, dims):
+    """Decode equals the prefill kernel with one query row (causal is a no-op
+    there) and both equal the oracle."""
+    import online_softmax_05_amd as fa
+
+    dk, dv = dims
+    g = torch.Generator().manual_seed(dk * 1000 + dv)
+    B, H, Nk = 3, 2, 777
+    q = torch.randn(B, H, 1, dk, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, dk, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, dv, generator=g).to(torch.bfloat16)
+    k_len = torch.tensor([777, 300, 64], dtype=torch.int32)
+    say(f"decode vs fwd dims={dims}")
+    qd, kd, vd, kl = q.to(dev), k.to(dev), v.to(dev), k_len.to(dev)
+    od, ld = fa.fa_decode_splitk(qd[:, :, 0].contiguous(), kd, vd, kl, chunk=128)
+    of, lf = fa.fa_fwd(qd, kd, vd, k_len=kl, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(f64(q), f64(k), f64(v), scale=scale32(1 / math.sqrt(dk)),
+                                          k_len=k_len.numpy())
+    compare(od[:, :, None], ld[:, :, None], o_ref, lse_ref, torch.bfloat16, f"decode dims={dims}")
+    compare(of, lf, o_ref, lse_ref, torch.bfloat16, f"fwd Nq=1 dims={dims}")
+
+
+def test_decode_empty_and_degenerate(dev):
+    import online_softmax_05_amd as fa
+
+    say("decode degenerate")
+    q = torch.randn(2, 2, 64, device=dev).to(torch.bfloat16)
+    k = torch.randn(2, 2, 0, 64, device=dev).to(torch.bfloat16)
+    o, lse = fa.fa_decode_splitk(q, k, k, torch.tensor([0, 5], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    # Nk = 0 prefill: o = 0, lse = -inf
+    qq = torch.randn(1, 2, 9, 16, device=dev)
+    kk = torch.randn(1, 2, 0, 16, device=dev)
+    o, lse = fa.fa_fwd(qq, kk, kk)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
