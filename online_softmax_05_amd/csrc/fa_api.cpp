@@ -108,8 +108,12 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, const
   if (st != FA_OK) return st;
   if ((long long)B * H * Nq == 0) return FA_OK;
   fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal, block_n == 0 ? 64 : block_n};
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, static_cast<hipStream_t>(stream))
-                                        : fa::launch_fwd_f32(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_BF16)
+    e = fa::fwd_bf16_fast_eligible(a) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
+  else
+    e = fa::launch_fwd_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

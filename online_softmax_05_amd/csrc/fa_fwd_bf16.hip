@@ -46,6 +46,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per work-group
+constexpr float kRebase = 8.f;    // lazy rebasing threshold (log2 units)
 
 template <int DK, int DV, int BN>
 struct Tile {
@@ -180,13 +181,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int kend = visible_key_end(klen, causal != 0, last_row, Nq, Nk);
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
+  // Logit scale in the base-2 domain, made positive: a negative scale flips
+  // the sign of Q instead (exact in bf16), and a zero scale is replaced by a
+  // tiny positive one whose products with finite dot products round to 0 in
+  // every exponent.
+  const bool neg_scale = scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(scale_log2), 1e-30f);
+
   // Q^T fragment: B operand, k-step t holds dims 16t + 8*hf .. +7 of row qi
   bf16x8 qf[DK / 16];
   {
     const uint16_t* qrow = qbh + (size_t)(row_valid ? qi : 0) * dk;
+    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
       u32x4 w = row_valid ? load_row8(qrow, 16 * t + 8 * hf, dk, vec_q != 0) : u32x4{0u, 0u, 0u, 0u};
+      w[0] ^= flip; w[1] ^= flip; w[2] ^= flip; w[3] ^= flip;
       qf[t] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -229,7 +239,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     // ---- scale (+ bias) and mask, in the base-2 domain ---------------------
-    // accumulator register r of key block kb holds key n0 + 32kb + 8(r/4) + 4hf + r%4
+    // Accumulator register r of key block kb holds key n0 + 32kb + 8(r/4) +
+    // 4hf + r%4.  Without a bias s[] keeps the raw dot products: the scale
+    // c > 0 is folded into one FMA in the exponent and max(c s) = c max(s).
+    // With a bias s[] keeps c s and the biased logit only feeds the maximum;
+    // the exponent re-adds the bias after subtracting the maximum, so large
+    // bias values cancel before rounding.
     const bool need_mask = n0 + BN > wave_min_end;
     float mx = kNegInf;
 #pragma unroll
@@ -241,44 +256,56 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (BIAS) bv = load_bias4(brow, key0, Nk, vec_bias != 0, row_valid);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // s[] keeps scale*log2e*(q.k) (or -inf); with a bias the biased
-          // logit only feeds the maximum, and the exponent below re-adds the
-          // bias after subtracting the maximum, so large bias values cancel
-          // before rounding
           const bool masked = need_mask && key0 + j >= row_end;
-          const float sc = masked ? kNegInf : s[kb][4 * i + j] * scale_log2;
-          s[kb][4 * i + j] = sc;
-          mx = fmaxf(mx, BIAS ? sc + bv[j] * kLog2e : sc);
+          if (BIAS) {
+            const float sc = masked ? kNegInf : s[kb][4 * i + j] * c;
+            s[kb][4 * i + j] = sc;
+            mx = fmaxf(mx, sc + bv[j] * kLog2e);
+          } else {
+            const float x = masked ? kNegInf : s[kb][4 * i + j];
+            s[kb][4 * i + j] = x;
+            mx = fmaxf(mx, x);
+          }
         }
       }
     }
+    if (!BIAS) mx *= c;
 
-    // ---- running max, rescale factor, exponentials -------------------------
+    // ---- running reference, rescale factor, exponentials -----------------
+    // The reference m_run is moved only when this tile's maximum exceeds it
+    // by more than kRebase (log2 units); in between, exponentials are taken
+    // against the lagging reference and stay <= 2^kRebase.  Any common
+    // origin gives the same o = u / l, so l and u stay exact; rebasing both
+    // by alpha = exp2(m_old - m_new) when the reference moves keeps the state
+    // consistent ([GS] section 4).  An empty row keeps m_run = -inf.
     mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // empty so far: nothing to shift
-    const float alpha = fast_exp2(m_run - m_use);            // 0 for the empty state
+    const bool grow = mx > m_run + kRebase;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 for the empty state
     m_run = m_new;
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
 
     float psum = 0.f;
     bf16x8 pb[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
-      float xo[16];  // exponent offsets: -m, or bias*log2e - m
+      float xo[16];  // bias * log2e - m (bias path only)
+      if (BIAS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-        if (BIAS) bv = load_bias4(brow, n0 + kb * 32 + 8 * i + 4 * hf, Nk, vec_bias != 0, row_valid);
+        for (int i = 0; i < 4; ++i) {
+          f32x4 bv = load_bias4(brow, n0 + kb * 32 + 8 * i + 4 * hf, Nk, vec_bias != 0, row_valid);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xo[4 * i + j] = BIAS ? fmaf(bv[j], kLog2e, -m_use) : -m_use;
+          for (int j = 0; j < 4; ++j) xo[4 * i + j] = fmaf(bv[j], kLog2e, -m_use);
+        }
       }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          float p0 = fast_exp2(s[kb][8 * t2 + e] + xo[8 * t2 + e]);
-          float p1 = fast_exp2(s[kb][8 * t2 + e + 1] + xo[8 * t2 + e + 1]);
+          const int r0 = 8 * t2 + e, r1 = r0 + 1;
+          const float p0 = fast_exp2(BIAS ? s[kb][r0] + xo[r0] : fmaf(s[kb][r0], c, -m_use));
+          const float p1 = fast_exp2(BIAS ? s[kb][r1] + xo[r1] : fmaf(s[kb][r1], c, -m_use));
           psum += p0 + p1;
           w[e / 2] = pack_bf16x2(p0, p1);
         }
@@ -287,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     l_run = fmaf(alpha, l_run, psum);
 
-    // rescale u only when some row's maximum rose (alpha == 1 otherwise)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    // rescale u only when some row of the wave moved its reference
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d)
 #pragma unroll

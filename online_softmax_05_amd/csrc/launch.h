@@ -37,6 +37,9 @@ struct DecodeArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// fast bf16 path: head dims 64/128, 16-byte aligned tensors, 64-key tiles
+bool fwd_bf16_fast_eligible(const FwdArgs& a);
+hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);

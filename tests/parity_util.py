@@ -37,10 +37,16 @@ def oracle_full(inp):
                                 causal=inp["causal"], k_len=k_len, bias=f64(inp.get("bias")))
 
 
-def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None):
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None, logit_scale=1.0):
     """Max-abs comparison at the dtype's tolerance; rows with lse_ref = -inf
-    (empty rows) must match exactly: o = 0 and lse = -inf."""
-    tol = TOL[dtype]
+    (empty rows) must match exactly: o = 0 and lse = -inf.
+
+    ``logit_scale`` >= 1 widens the fp32 bounds for logits larger than the
+    standard scaling gives: fp32 represents a logit of size |s| only to about
+    |s| * 6e-8, so both fp32 bounds grow in proportion."""
+    tol = dict(TOL[dtype])
+    if dtype == torch.float32 and logit_scale > 1.0:
+        tol = dict(o=tol["o"] * logit_scale, lse=tol["lse"] * logit_scale)
     o = f64(o_gpu)
     lse = f64(lse_gpu)
     assert o.shape == o_ref.shape, (what, o.shape, o_ref.shape)

@@ -198,6 +198,23 @@ def test_seeded_sweep(dev, case):
     compare(o, lse, o_ref, lse_ref, DT[dt], f"sweep {n}")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-3, 3.0])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_scale_values(dev, scale, dt):
+    """Negative, zero, tiny and large logit scales (the kernels keep their
+    exponent scale positive by flipping the sign of Q)."""
+    for use_bias in (False, True):
+        inp = workloads.seeded_case(int(abs(scale) * 1000) + 3, 2, 2, 150, 140, 64, 64, DT[dt], causal=True,
+                                    bias=use_bias, k_len=[140, 77])
+        inp["scale"] = scale
+        say(f"scale={scale} {dt} bias={use_bias}")
+        o, lse = run_fwd(inp, dev)
+        o_ref, lse_ref = oracle_full(inp)
+        # logits here are up to |scale| sqrt(dk) times the standard scaling's
+        compare(o, lse, o_ref, lse_ref, DT[dt], f"scale={scale} {dt} bias={use_bias}",
+                logit_scale=max(1.0, abs(scale) * math.sqrt(64)))
+
+
 def test_k_len_clamped(dev):
     """k_len outside [0, Nk] is clamped by the kernels."""
     inp = workloads.seeded_case(31, 3, 2, 40, 50, 64, 64, torch.bfloat16, causal=False, k_len=[-5, 77, 20])
