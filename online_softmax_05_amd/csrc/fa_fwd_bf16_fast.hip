@@ -17,8 +17,9 @@
 // * Key tiles of 64 keys.  K and V tiles go from global memory straight into
 //   LDS (global_load_lds_dwordx4: no staging registers, no LDS store
 //   instructions), row-major, with the 16-byte chunks of row r stored at
-//   chunk index c ^ (r & 7) so that the 16 rows one MFMA operand read
-//   touches fall in distinct LDS banks.
+//   chunk index c ^ (r & 7) so that the rows one MFMA operand read touches
+//   fall in distinct LDS banks.  Every operand address is then a per-lane
+//   base (2 for K, 4 for V) plus a compile-time offset.
 // * The matrix products use v_mfma_f32_16x16x32_bf16.  Each wave computes
 //   S^T = K Q^T: a lane of the 16x16 accumulator holds one query and four
 //   consecutive keys, so the row maximum is an in-lane max plus two lane
@@ -28,10 +29,14 @@
 //   group, four lanes point at 8-byte pieces of four key rows and every lane
 //   receives one dim of all four keys -- the transpose happens in the LDS
 //   read, so V stays in its natural row-major order.
-// * Software pipeline: K runs one tile ahead of V.  While the softmax of
-//   tile t runs on the VALU, the MFMAs of S^T for tile t+1 are issued; the
-//   loads of K_{t+2} and V_{t+1} are in flight during the whole iteration,
-//   and one barrier per iteration publishes them.
+// * Row sums of P are taken in fp32 before P is rounded to bf16 (a sum of
+//   the rounded values on the matrix cores would leave ~1e-3 relative
+//   error in l, and so in lse, on rows dominated by a few keys).
+// * Double buffering: the loads of tile t+1 are in flight during the whole
+//   of tile t, and one barrier per tile publishes them.  Two work-groups
+//   share each CU, so one wave's softmax (VALU) overlaps the other wave's
+//   matrix products on the same SIMD.  Tiles that need no mask for any row
+//   of the work-group run a variant without mask code.
 //
 // Online state per query row (base-2 domain): reference m (moved lazily,
 // only when the tile maximum exceeds it by more than 8), denominator l and
@@ -51,49 +56,24 @@ constexpr int kBM = 32 * kWaves;  // query rows per work-group
 constexpr int kBN = 64;           // keys per tile
 constexpr float kRebase = 8.f;    // lazy rebasing threshold (log2 units)
 
+// Pace LDS operand reads against the MFMAs that consume them (bounds the
+// registers held by fragments in flight).
+#ifndef FA_FAST_PACE
+#define FA_FAST_PACE 1
+#endif
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef const __attribute__((address_space(1))) void gbl_void;
 typedef __attribute__((address_space(3))) void lds_void;
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// Tile of kBN rows x D bf16 in LDS: R 16-byte chunks per row, chunk c of row
-// r at position c ^ (r & 7).
-template <int D>
-struct SwzTile {
-  static constexpr int R = D / 8;
-  static constexpr int BYTES = kBN * D * 2;
-  static constexpr int INSTS = kBN * R / 64;            // 1 KiB wave-wide loads per tile
-  static constexpr int INSTS_PER_WAVE = INSTS / kWaves;
-  static_assert(R >= 8 && INSTS % kWaves == 0, "tile shape");
-  __device__ static __forceinline__ int off(int row, int c) { return (row * R + (c ^ (row & 7))) * 16; }
-};
-
-// Issue the direct-to-LDS loads of one tile (this wave's share).  Rows past
-// the last key re-read the last key row (finite values whose probabilities
-// are zero), so no lane reads out of bounds.
-template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* gbh, int n0, int nk, lds_char* tile, int wave, int lane) {
-  using T = SwzTile<D>;
-#pragma unroll
-  for (int i = 0; i < T::INSTS_PER_WAVE; ++i) {
-    const int inst = wave * T::INSTS_PER_WAVE + i;
-    const int slot = inst * 64 + lane;
-    const int row = slot / T::R;
-    const int c = (slot % T::R) ^ (row & 7);
-    const int grow = min(n0 + row, nk - 1);
-    const uint16_t* g = gbh + (size_t)grow * D + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)(tile + inst * 1024), 16, 0, 0);
-  }
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -112,6 +92,72 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Tile of kBN rows x D bf16 in LDS: R 16-byte chunks per row, chunk c of row
+// r at chunk position c ^ (r & 7).
+template <int D>
+struct SwzTile {
+  static constexpr int R = D / 8;
+  static constexpr int ROW = R * 16;                 // bytes per row
+  static constexpr int BYTES = kBN * ROW;
+  static constexpr int IPW = kBN * R / 64 / kWaves;  // 1 KiB wave-wide loads per wave per tile
+  static_assert(R >= 8 && kBN * R % (64 * kWaves) == 0, "tile shape");
+};
+
+// Per-lane parts of every address the kernel forms.
+template <int DK, int DV>
+struct LaneAddr {
+  int k[2];                   // K fragment base, k-step parity t & 1
+  int v[4];                   // V^T transposed-read base, dim block db & 3
+  int kld[SwzTile<DK>::IPW];  // element offset (row * DK + chunk * 8) of each direct K load
+  int vld[SwzTile<DV>::IPW];
+
+  __device__ __forceinline__ void init(int lane, int wave) {
+    const int r16 = lane & 15, g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
+    // K fragment (key block kb, k-step t): row 16kb + r16, chunk 4t + g; with
+    // x = r16 & 7 the swizzled chunk is 8(t/2) + ((g ^ x) ^ 4(t & 1)).
+    const int x = r16 & 7;
+    k[0] = r16 * SwzTile<DK>::ROW + 16 * (g ^ x);
+    k[1] = r16 * SwzTile<DK>::ROW + 16 * ((g ^ x) ^ 4);
+    // V^T read (dim block db, key row 32kt + 16h + 4g + e, bytes 8(r & 1)
+    // of chunk 2db + r/2): with z = (4g + e) & 7 the swizzled chunk is
+    // 8(db / 4) + ((2(db % 4) + r/2) ^ z).
+    const int z = (4 * g + e) & 7;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      v[b] = (4 * g + e) * SwzTile<DV>::ROW + 16 * ((2 * b + (r >> 1)) ^ z) + 8 * (r & 1);
+#pragma unroll
+    for (int i = 0; i < SwzTile<DK>::IPW; ++i) {
+      const int slot = (wave * SwzTile<DK>::IPW + i) * 64 + lane;
+      const int row = slot / SwzTile<DK>::R;
+      kld[i] = row * DK + ((slot % SwzTile<DK>::R) ^ (row & 7)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < SwzTile<DV>::IPW; ++i) {
+      const int slot = (wave * SwzTile<DV>::IPW + i) * 64 + lane;
+      const int row = slot / SwzTile<DV>::R;
+      vld[i] = row * DV + ((slot % SwzTile<DV>::R) ^ (row & 7)) * 8;
+    }
+  }
+};
+
+// Direct-to-LDS loads of this wave's share of one tile whose first key row
+// is `tile` (rows_left keys remain in the tensor from there).  Rows past the
+// last key re-read the last key row (finite values whose probabilities are
+// zero), so no lane reads out of bounds.
+template <int D, int IPW>
+__device__ __forceinline__ void load_tile(const uint16_t* tile, int rows_left, const int (&ld)[IPW], lds_char* dst,
+                                          int wave) {
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    int off = ld[i];
+    if (rows_left < kBN) {
+      const int row = off / D;
+      if (row >= rows_left) off += (rows_left - 1 - row) * D;
+    }
+    __builtin_amdgcn_global_load_lds((gbl_void*)(tile + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
+  }
+}
+
 template <int DK>
 struct QFrag {
   bf16x8 f[2][DK / 32];  // [query block][k-step]: dims 32t + 8g .. +7
@@ -120,63 +166,73 @@ struct QFrag {
 // S^T (keys x queries) of one tile: s[kb][qb] is the 16x16 block of key
 // block kb and query block qb; a lane holds keys 16kb + 4g + j of query
 // 16qb + lane % 16.
-template <int DK>
-__device__ __forceinline__ void qk_tile(f32x4 (&s)[4][2], const QFrag<DK>& q, const lds_char* kt, int lane) {
-  using T = SwzTile<DK>;
-  const int r16 = lane & 15, g = lane >> 4;
+template <int DK, int DV>
+__device__ __forceinline__ void qk_tile(f32x4 (&s)[4][2], const QFrag<DK>& q, const lds_char* kt,
+                                        const LaneAddr<DK, DV>& la) {
+  constexpr int ROW = SwzTile<DK>::ROW;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DK / 32; ++t) {
-      const bf16x8 a = *(const lds_bf16x8*)(kt + T::off(16 * kb + r16, 4 * t + g));
+      const bf16x8 a = *(const lds_bf16x8*)(kt + la.k[t & 1] + 16 * kb * ROW + 128 * (t >> 1));
       s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.f[0][t], s[kb][0], 0, 0, 0);
       s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.f[1][t], s[kb][1], 0, 0, 0);
     }
   }
+#if FA_FAST_PACE
+  // keep at most two K fragments in flight: read, read, then (2 MFMAs, read)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+  for (int i = 0; i < 4 * DK / 32; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    if (i + 2 < 4 * DK / 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+  }
+#endif
 }
 
-// O^T += V^T P^T for one tile: k-step T covers keys 32T .. 32T+31, slot s of
-// lane group g holding key 32T + 16(s/4) + 4g + s%4.
-template <int DV>
+struct RowState {
+  float m[2];  // reference maximum (base 2) per query block
+  float l[2];  // this lane's share (4 of the 64 keys of each tile) of the denominator
+};
+
+// O^T += V^T P^T for one tile: k-step kt covers keys 32kt .. 32kt+31, slot
+// s of lane group g holding key 32kt + 16(s/4) + 4g + s%4.
+template <int DK, int DV>
 __device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&pb)[2][2], const lds_char* vt,
-                                        int lane) {
-  using T = SwzTile<DV>;
-  const int g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
+                                        const LaneAddr<DK, DV>& la) {
+  constexpr int ROW = SwzTile<DV>::ROW;
 #pragma unroll
   for (int db = 0; db < DV / 16; ++db) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      v4i16 lo, hi;
-      {
-        const int row = 32 * kt + 4 * g + e;
-        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(vt + T::off(row, 2 * db + (r >> 1)) + 8 * (r & 1)));
-        const int row2 = row + 16;
-        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(vt + T::off(row2, 2 * db + (r >> 1)) + 8 * (r & 1)));
-      }
+      const lds_char* p = vt + la.v[db & 3] + 32 * kt * ROW + 128 * (db >> 2);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * ROW));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kt][0], o[db][0], 0, 0, 0);
       o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kt][1], o[db][1], 0, 0, 0);
     }
   }
+#if FA_FAST_PACE
+  // per V fragment: 2 transposed reads, 2 MFMAs, one fragment read ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+#pragma unroll
+  for (int i = 0; i < DV / 8; ++i) {
+    if (i + 1 < DV / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+  }
+#endif
 }
 
-struct RowState {
-  float m[2];  // reference maximum (base 2) per query block
-  float l[2];  // this lane's share of the denominator
-};
-
-// Softmax of one tile in place: mask, running reference, exponentials, P in
-// bf16, and the rescale factors.  Returns in alpha[qb] the factor the value
-// sums must be multiplied by, and whether any row of the wave moved.
+// Softmax of one tile in place: mask, running reference, exponentials and P
+// in bf16.  alpha[qb] receives the factor the value sums must be multiplied
+// by; the return value says whether any row of the wave moved its reference.
 template <bool MASK, bool BIAS>
 __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2], RowState& st, float (&alpha)[2],
                                              float c, int n0, const int (&row_end)[2], const float* const (&brow)[2],
-                                             const bool (&rvalid)[2], int nk, bool vec_bias, int lane) {
-  const int g = lane >> 4;
+                                             const bool (&rvalid)[2], int nk, bool vec_bias, int g) {
   float xo[2][4][4];  // bias path: the raw bias per element
   float mx[2];
 #pragma unroll
@@ -246,6 +302,53 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
 }
 
 template <int DK, int DV, bool BIAS>
+struct FwdTile {
+  // inputs of this work-group
+  const uint16_t* kbh;
+  const uint16_t* vbh;
+  int nk, n_tiles;
+  float c;
+  int row_end[2];
+  bool rvalid[2];
+  const float* brow[2];
+  int vec_bias, g;
+  // per-thread state
+  LaneAddr<DK, DV> la;
+  QFrag<DK> qf;
+  f32x4 o[DV / 16][2];
+  RowState st;
+
+  // One tile t (K_t and V_t in kcur / vcur) while tile t+1 loads into
+  // knext / vnext: S^T, softmax, rescale, O += P V, then the barrier that
+  // publishes tile t+1 and frees tile t's buffers.
+  template <bool MASK>
+  __device__ __forceinline__ void step(int t, int wave, const lds_char* kcur, const lds_char* vcur,
+                                       lds_char* knext, lds_char* vnext) {
+    const int n0 = t * kBN;
+    if (t + 1 < n_tiles) {
+      load_tile<DK>(kbh + (size_t)(n0 + kBN) * DK, nk - (n0 + kBN), la.kld, knext, wave);
+      load_tile<DV>(vbh + (size_t)(n0 + kBN) * DV, nk - (n0 + kBN), la.vld, vnext, wave);
+    }
+    f32x4 s[4][2];
+    qk_tile<DK, DV>(s, qf, kcur, la);
+    bf16x8 pb[2][2];
+    float alpha[2];
+    const bool grow =
+        softmax_tile<MASK, BIAS>(s, pb, st, alpha, c, n0, row_end, brow, rvalid, nk, vec_bias != 0, g);
+    if (grow) {
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d) {
+        o[d][0] *= alpha[0];
+        o[d][1] *= alpha[1];
+      }
+    }
+    pv_tile<DK, DV>(o, pb, vcur, la);
+    wait_loads();
+    __syncthreads();
+  }
+};
+
+template <int DK, int DV, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
@@ -254,6 +357,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   __shared__ __attribute__((aligned(1024))) char kbuf1[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[SwzTile<DV>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf1[SwzTile<DV>::BYTES];
+  lds_char* K0 = (lds_char*)kbuf0;
+  lds_char* K1 = (lds_char*)kbuf1;
+  lds_char* V0 = (lds_char*)vbuf0;
+  lds_char* V1 = (lds_char*)vbuf1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -266,121 +373,99 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int klen = clamp_klen(k_len, b, Nk);
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
-  const uint16_t* kbh = k + bh * Nk * DK;
-  const uint16_t* vbh = v + bh * Nk * DV;
+
+  FwdTile<DK, DV, BIAS> ft;
+  ft.kbh = k + bh * Nk * DK;
+  ft.vbh = v + bh * Nk * DV;
+  ft.nk = Nk;
+  ft.vec_bias = vec_bias;
+  ft.g = g;
+  ft.la.init(lane, wave);
 
   const int shift = Nk - Nq;
-  int qrow[2], row_end[2];
-  bool rvalid[2];
-  const float* brow[2];
+  int qrow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     qrow[qb] = q0 + wave * 32 + qb * 16 + r16;
-    rvalid[qb] = qrow[qb] < Nq;
-    row_end[qb] = causal ? min(klen, qrow[qb] + shift + 1) : klen;
-    brow[qb] = BIAS ? bias + (bh * Nq + (size_t)(rvalid[qb] ? qrow[qb] : 0)) * Nk : nullptr;
+    ft.rvalid[qb] = qrow[qb] < Nq;
+    ft.row_end[qb] = causal ? min(klen, qrow[qb] + shift + 1) : klen;
+    ft.brow[qb] = BIAS ? bias + (bh * Nq + (size_t)(ft.rvalid[qb] ? qrow[qb] : 0)) * Nk : nullptr;
   }
-  const int wave_first = q0 + wave * 32;
-  const int wave_min_end = causal ? min(klen, wave_first + shift + 1) : klen;
   const int kend = visible_key_end(klen, causal != 0, min(q0 + kBM, Nq) - 1, Nq, Nk);
   const int n_tiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
+  ft.n_tiles = n_tiles;
 
   // logit scale in the base-2 domain, made positive (a negative scale flips
   // the sign of Q, exactly; zero becomes a tiny positive value)
   const bool neg_scale = scale_log2 < 0.f;
-  const float c = fmaxf(fabsf(scale_log2), 1e-30f);
-
-  QFrag<DK> qf;
+  ft.c = fmaxf(fabsf(scale_log2), 1e-30f);
   {
     const uint32_t flip = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const uint16_t* qr = qbh + (size_t)(rvalid[qb] ? qrow[qb] : 0) * DK;
+      const uint16_t* qr = qbh + (size_t)(ft.rvalid[qb] ? qrow[qb] : 0) * DK;
 #pragma unroll
       for (int t = 0; t < DK / 32; ++t) {
-        u32x4 w = rvalid[qb] ? *reinterpret_cast<const u32x4*>(qr + 32 * t + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+        u32x4 w = ft.rvalid[qb] ? *reinterpret_cast<const u32x4*>(qr + 32 * t + 8 * g) : u32x4{0u, 0u, 0u, 0u};
         w[0] ^= flip; w[1] ^= flip; w[2] ^= flip; w[3] ^= flip;
-        qf.f[qb][t] = __builtin_bit_cast(bf16x8, w);
+        ft.qf.f[qb][t] = __builtin_bit_cast(bf16x8, w);
       }
     }
   }
-
-  f32x4 oacc[DV / 16][2];
 #pragma unroll
   for (int d = 0; d < DV / 16; ++d) {
-    oacc[d][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    oacc[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ft.o[d][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ft.o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  RowState st;
-  st.m[0] = st.m[1] = kNegInf;
-  st.l[0] = st.l[1] = 0.f;
+  ft.st.m[0] = ft.st.m[1] = kNegInf;
+  ft.st.l[0] = ft.st.l[1] = 0.f;
 
-  f32x4 s_cur[4][2];
   if (n_tiles > 0) {
-    load_tile<DK>(kbh, 0, Nk, (lds_char*)kbuf0, wave, lane);
-    load_tile<DV>(vbh, 0, Nk, (lds_char*)vbuf0, wave, lane);
-    if (n_tiles > 1) load_tile<DK>(kbh, kBN, Nk, (lds_char*)kbuf1, wave, lane);
+    load_tile<DK>(ft.kbh, Nk, ft.la.kld, K0, wave);
+    load_tile<DV>(ft.vbh, Nk, ft.la.vld, V0, wave);
     wait_loads();
     __syncthreads();
-    qk_tile<DK>(s_cur, qf, (const lds_char*)kbuf0, lane);
-    __syncthreads();  // every wave has read K_0 before K_2 replaces it
-  }
 
-  // One pipelined iteration: loads of K_{t+2} and V_{t+1} in flight, S^T of
-  // tile t+1 computed beside the softmax of tile t, then O += P_t V_t.
-  auto iterate = [&](int t, lds_char* kdst, const lds_char* knext, const lds_char* vcur, lds_char* vdst) {
-    const int n0 = t * kBN;
-    if (t + 2 < n_tiles) load_tile<DK>(kbh, n0 + 2 * kBN, Nk, kdst, wave, lane);
-    if (t + 1 < n_tiles) load_tile<DV>(vbh, n0 + kBN, Nk, vdst, wave, lane);
-    f32x4 s_next[4][2];
-    qk_tile<DK>(s_next, qf, knext, lane);  // garbage (never used) after the last tile
-    bf16x8 pb[2][2];
-    float alpha[2];
-    bool grow;
-    if (n0 + kBN > wave_min_end)
-      grow = softmax_tile<true, BIAS>(s_cur, pb, st, alpha, c, n0, row_end, brow, rvalid, Nk, vec_bias != 0, lane);
-    else
-      grow = softmax_tile<false, BIAS>(s_cur, pb, st, alpha, c, n0, row_end, brow, rvalid, Nk, vec_bias != 0, lane);
-    if (grow) {
-#pragma unroll
-      for (int d = 0; d < DV / 16; ++d) {
-        oacc[d][0] *= alpha[0];
-        oacc[d][1] *= alpha[1];
-      }
+    // Tiles before the work-group's first row's visible end need no mask
+    // for any of its rows; the rest (the causal diagonal, the key-length
+    // boundary) run the masked variant.  Buffers alternate with the parity
+    // of the tile index.
+    const int wg_first_end = causal ? min(klen, q0 + shift + 1) : klen;
+    const int n_full = min(n_tiles, max(wg_first_end, 0) / kBN);
+    int t = 0;
+    for (; t + 1 < n_full; t += 2) {
+      ft.template step<false>(t, wave, K0, V0, K1, V1);
+      ft.template step<false>(t + 1, wave, K1, V1, K0, V0);
     }
-    pv_tile<DV>(oacc, pb, vcur, lane);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s_cur[kb][0] = s_next[kb][0];
-      s_cur[kb][1] = s_next[kb][1];
+    if (t < n_full) {
+      ft.template step<false>(t, wave, K0, V0, K1, V1);
+      ++t;
     }
-    wait_loads();
-    __syncthreads();
-  };
-
-  for (int t = 0; t < n_tiles; t += 2) {
-    iterate(t, (lds_char*)kbuf0, (const lds_char*)kbuf1, (const lds_char*)vbuf0, (lds_char*)vbuf1);
-    if (t + 1 < n_tiles)
-      iterate(t + 1, (lds_char*)kbuf1, (const lds_char*)kbuf0, (const lds_char*)vbuf1, (lds_char*)vbuf0);
+    for (; t < n_tiles; ++t) {
+      if (t & 1)
+        ft.template step<true>(t, wave, K1, V1, K0, V0);
+      else
+        ft.template step<true>(t, wave, K0, V0, K1, V1);
+    }
   }
 
   // ---- epilogue: divide once; empty rows get o = 0, lse = -inf ------------
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = quad_sum(st.l[qb]);
-    if (!rvalid[qb]) continue;
+    const float l_tot = quad_sum(ft.st.l[qb]);
+    if (!ft.rvalid[qb]) continue;
     const bool nonempty = l_tot > 0.f;
     const float inv = nonempty ? 1.f / l_tot : 0.f;
     uint16_t* orow = o + (bh * Nq + qrow[qb]) * (size_t)DV;
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
       u32x2 w;
-      w[0] = cvt_pk_bf16(oacc[d][qb][0] * inv, oacc[d][qb][1] * inv);
-      w[1] = cvt_pk_bf16(oacc[d][qb][2] * inv, oacc[d][qb][3] * inv);
+      w[0] = cvt_pk_bf16(ft.o[d][qb][0] * inv, ft.o[d][qb][1] * inv);
+      w[1] = cvt_pk_bf16(ft.o[d][qb][2] * inv, ft.o[d][qb][3] * inv);
       *reinterpret_cast<u32x2*>(orow + 16 * d + 4 * g) = w;
     }
     if (lse != nullptr && g == 0)
-      lse[bh * Nq + qrow[qb]] = nonempty ? (st.m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
+      lse[bh * Nq + qrow[qb]] = nonempty ? (ft.st.m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -405,7 +490,7 @@ hipError_t launch_b(const FwdArgs& a, hipStream_t s) {
 bool fwd_bf16_fast_eligible(const FwdArgs& a) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && a.Nk > 0 && aligned(a.q) &&
-         aligned(a.k) && aligned(a.v) && aligned(a.o) && (a.block_n == 0 || a.block_n == kBN);
+         aligned(a.k) && aligned(a.v) && aligned(a.o) && a.block_n == kBN;
 }
 
 hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t s) {
