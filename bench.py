@@ -44,17 +44,24 @@ sys.path.insert(0, str(ROOT))
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk (dense bf16 MFMA) x 2.4 GHz (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0      # HBM3E, published 8 TB/s
 METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s (% peak)"
-KERNEL_SOURCES = ["online_softmax_05_amd/csrc/fa_fwd_bf16.hip", "online_softmax_05_amd/csrc/fa_decode.hip",
-                  "online_softmax_05_amd/csrc/fa_common.h"]
+# sources of the kernel each workload's roofline describes (stored counter
+# summaries are only reported while these still hash to the recorded value)
+KERNEL_SOURCES = {
+    "prefill": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+    "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+    "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+}
+KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
+                "decode": "decode_partial_kernel<unsigned short, 128, 128> + decode_merge_kernel"}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(name):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[name]:
         h.update((ROOT / rel).read_bytes())
     return h.hexdigest()[:16]
 
@@ -72,7 +79,7 @@ def stored_traffic(name):
     if not p.exists():
         return None
     rec = json.loads(p.read_text())
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(name):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -214,7 +221,7 @@ def run_prefill(name, args, dev):
         frac_of_peak=value / PEAK_BF16_TFLOPS,
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
-                      kernel="fwd_bf16_kernel<128,128,64,false>", launch_ms_mean=t["launch_ms_mean"],
+                      kernel=KERNEL_NAMES[name], launch_ms_mean=t["launch_ms_mean"],
                       launch_ms_median=t["launch_ms_median"], algorithmic_flops_per_launch=flops,
                       algorithmic_bytes_per_launch=2 * B * H * N * (2 * dk + dv) + 2 * B * H * N * dv
                       + 4 * B * H * N),
@@ -261,7 +268,7 @@ def run_decode(args, dev):
         workload=workloads.DESCRIPTIONS["decode"], value=value, unit="GB/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
-                      traffic=stored_traffic("decode"), kernel="decode_partial_kernel + decode_merge_kernel",
+                      traffic=stored_traffic("decode"), kernel=KERNEL_NAMES["decode"],
                       launch_ms_mean=t["launch_ms_mean"], launch_ms_median=t["launch_ms_median"],
                       algorithmic_bytes_per_launch=nbytes),
         config=dict(workload=workloads.DESCRIPTIONS["decode"], B=B, H=H, Nk_max=Nk, dk=dk, dv=dv, chunk=chunk,
@@ -342,7 +349,7 @@ def main():
         "roofline": main_res["roofline"],
         "cpu_baseline": main_res.get("cpu_baseline"),
         "secondary": [dict(results[w]) for w in order[1:]],
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": {w: kernel_source_hash(w) for w in order},
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
