@@ -210,6 +210,172 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   if (lse != nullptr && lane == 0) lse[bhi] = nonempty ? (m + fast_log2(l)) * kLn2 : kNegInf;
 }
 
+// ---------------------------------------------------------------------------
+// Fast partial kernel for bf16 with dk = dv = 128 and 16-byte aligned
+// tensors.  One pass streams K and V together: each 256-byte key row is
+// spread over 16 lanes (16 bytes each) and four consecutive rows fill a
+// wave-wide load, so K and V rows sit in the same lanes and the probability
+// of a row is already in the lanes that hold its value row.  Each of the
+// four 16-lane row groups of a wave keeps its own online state (m, l, u)
+// over the rows it sees (the pages' sequential update, [GS] section 5);
+// the states are merged once at the end -- across the row groups, then
+// across the waves through LDS -- with the rule of [GS] section 4.
+// Work-groups are numbered chunk-major, so the (b, h, chunk) triples past a
+// sequence's length -- which exit at once -- cluster at the end of the grid.
+constexpr int kFastD = 128;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 16 lanes of a DPP row: xor 1, xor 2, then mirrors
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Taking the element by value matters: a bit cast applied directly to an
+// indexed element of a vector held by reference was lowered as a cast of
+// element 0.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2_t, x); }
+
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b) {
+  float d = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[p]), as_bf16x2(b[p]), d, false);
+  return d;
+}
+
+struct DecState {
+  float m, l, u[8];
+};
+
+// merge with the state held by lane ^ off ([GS] section 4); an empty state
+// (m = -inf) contributes nothing
+__device__ __forceinline__ void merge_lanes(DecState& st, int off) {
+  const float m_o = __shfl_xor(st.m, off);
+  const float l_o = __shfl_xor(st.l, off);
+  const float m_new = fmaxf(st.m, m_o);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float a = fast_exp2(st.m - m_use), bo = fast_exp2(m_o - m_use);
+  st.l = a * st.l + bo * l_o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.u[e] = a * st.u[e] + bo * __shfl_xor(st.u[e], off);
+  st.m = m_new;
+}
+
+__global__ __launch_bounds__(kThreads) void decode_partial_fast_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ k_len, float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int BH, int Nk,
+    int chunk, int max_chunks, float scale_log2) {
+  constexpr int D = kFastD;
+  __shared__ float red_u[4][D];
+  __shared__ float red_ml[4][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x / BH;
+  const int bhi = blockIdx.x - c * BH;
+  const int b = bhi / H;
+  const int klen = clamp_klen(k_len, b, Nk);
+  const int c0 = c * chunk;
+  if (c0 >= klen) return;  // no allowed key in this chunk: no state
+  const int len = min(chunk, klen - c0);
+
+  const size_t bh = (size_t)bhi;
+  const int col = lane & 15, grp = lane >> 4;  // 16-byte column of a row; row group
+  const u32x4 qf = *reinterpret_cast<const u32x4*>(q + bh * D + col * 8);
+  const uint16_t* kp = k + (bh * Nk + c0) * D + col * 8;
+  const uint16_t* vp = v + (bh * Nk + c0) * D + col * 8;
+
+  // rows of this wave: one quarter of the chunk (a multiple of 16 rows)
+  const int quarter = chunk / 4;
+  const int r_begin = wave * quarter;
+  const int r_end = min(r_begin + quarter, len);
+
+  DecState st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.u[e] = 0.f;
+
+#pragma unroll 2
+  for (int r0 = r_begin; r0 < r_end; r0 += 16) {
+    u32x4 kv[4], vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * i + grp;
+      const bool ok = row < r_end;
+      kv[i] = ok ? *reinterpret_cast<const u32x4*>(kp + (size_t)row * D) : u32x4{0u, 0u, 0u, 0u};
+      vv[i] = ok ? *reinterpret_cast<const u32x4*>(vp + (size_t)row * D) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float sc[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = row16_sum(dot8_bf16(kv[i], qf));
+      sc[i] = (r0 + 4 * i + grp < r_end) ? d * scale_log2 : kNegInf;
+      mx = fmaxf(mx, sc[i]);
+    }
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    st.m = m_new;
+    float psum = 0.f;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(sc[i] - m_use);
+      psum += p[i];
+    }
+    st.l = fmaf(alpha, st.l, psum);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.u[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        st.u[2 * w] = fmaf(p[i], bf16_lo(vv[i][w]), st.u[2 * w]);
+        st.u[2 * w + 1] = fmaf(p[i], bf16_hi(vv[i][w]), st.u[2 * w + 1]);
+      }
+    }
+  }
+
+  // merge the four row groups of the wave, then the four waves
+  merge_lanes(st, 16);
+  merge_lanes(st, 32);
+  if (grp == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_u[wave][col * 8 + e] = st.u[e];
+    if (col == 0) {
+      red_ml[wave][0] = st.m;
+      red_ml[wave][1] = st.l;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, red_ml[w][0]);
+    float l = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fast_exp2(red_ml[w][0] - m);  // m is finite: the chunk holds a key
+      l = fmaf(a, red_ml[w][1], l);
+      u = fmaf(a, red_u[w][tid], u);
+    }
+    ws_u[(bh * max_chunks + c) * D + tid] = u;
+    if (tid == 0) {
+      float* wml = ws_ml + (bh * max_chunks + c) * 2;
+      wml[0] = m;
+      wml[1] = l;
+    }
+  }
+}
+
 template <typename T, int DKP, int DVP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int vec = Elem<T>::VEC;
@@ -240,7 +406,23 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) { return launch_d<uint16_t>(a, s); }
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool fast = a.dk == kFastD && a.dv == kFastD && aligned(a.q) && aligned(a.k) && aligned(a.v) &&
+                    a.chunk % 64 == 0;
+  if (!fast) return launch_d<uint16_t>(a, s);
+  const long long n_part = (long long)a.B * a.H * a.max_chunks;
+  if (n_part > 0) {
+    hipLaunchKernelGGL(decode_partial_fast_kernel, dim3((unsigned)n_part), dim3(kThreads), 0, s, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_len, a.ws_u, a.ws_ml, a.H, a.B * a.H, a.Nk,
+                       a.chunk, a.max_chunks, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<uint16_t>), dim3((unsigned)(a.B * a.H)), dim3(64), 0, s, a.ws_u, a.ws_ml,
+                     a.k_len, (uint16_t*)a.o, a.lse, a.H, a.Nk, a.dv, a.chunk, a.max_chunks);
+  return hipGetLastError();
+}
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_d<float>(a, s); }
 
 }  // namespace fa

@@ -354,6 +354,28 @@ def test_decode_small_full(dev, dt, chunk):
     compare(o[:, :, None], lse[:, :, None], o_ref, lse_ref, DT[dt], f"decode {dt} chunk={chunk}")
 
 
+@pytest.mark.parametrize("chunk", [64, 512, 2048])
+def test_decode_fast_path_lengths(dev, chunk):
+    """dk = dv = 128 bf16 (the single-pass partial kernel): lengths at and
+    around the 16-row steps, the 4-wave quarters and the chunk edges."""
+    import online_softmax_05_amd as fa
+
+    g = torch.Generator().manual_seed(900 + chunk)
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1000, 2047, 2048, 2049, 2500]
+    B, H, Nk, d = len(lens), 2, 2500, 128
+    q = torch.randn(B, H, d, generator=g).to(torch.bfloat16)
+    k = (torch.randn(B, H, Nk, d, generator=g) * 2.0).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    k_len = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    say(f"decode fast path chunk={chunk}")
+    o, lse = fa.fa_decode_splitk(q.to(dev), k.to(dev), v.to(dev), k_len.to(dev), scale=scale, chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(f64(q)[:, :, None], f64(k), f64(v), scale=scale32(scale),
+                                          k_len=k_len.numpy())
+    compare(o[:, :, None], lse[:, :, None], o_ref, lse_ref, torch.bfloat16, f"decode fast chunk={chunk}")
+
+
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (40, 24), (1, 1)])
 def test_decode_matches_fwd_nq1(dev, dims):
     """Decode equals the prefill kernel with one query row (causal is a no-op
