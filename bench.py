@@ -52,7 +52,7 @@ KERNEL_SOURCES = {
     "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
 }
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
-                "decode": "decode_partial_kernel<unsigned short, 128, 128> + decode_merge_kernel"}
+                "decode": "decode_partial_fast_kernel + decode_merge_kernel"}
 
 
 def log(msg):

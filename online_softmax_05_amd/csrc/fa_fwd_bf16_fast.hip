@@ -16,10 +16,15 @@
 //   First K/V Tile").
 // * Key tiles of 64 keys.  K and V tiles go from global memory straight into
 //   LDS (global_load_lds_dwordx4: no staging registers, no LDS store
-//   instructions), row-major, with the 16-byte chunks of row r stored at
-//   chunk index c ^ (r & 7) so that the rows one MFMA operand read touches
-//   fall in distinct LDS banks.  Every operand address is then a per-lane
-//   base (2 for K, 4 for V) plus a compile-time offset.
+//   instructions), row-major, with the 16-byte chunk c of row r stored at
+//   chunk index c ^ f(r).  The LDS serves a 128-bit read 16 lanes at a time
+//   and a 64-bit read 32 lanes at a time, each pass over 256 bytes of
+//   banks; f is chosen so that the 16 rows of a K-operand read land on 16
+//   distinct 16-byte bank positions and the 8 rows of a transposed V read
+//   (an aligned 32-byte chunk pair each) on 8 distinct pairs, i.e. every
+//   read takes the minimum number of passes.  Every operand address is then
+//   a per-lane base (one per k-step for K, one per 16-dim block for V) plus
+//   a compile-time offset.
 // * The matrix products use v_mfma_f32_16x16x32_bf16.  Each wave computes
 //   S^T = K Q^T: a lane of the 16x16 accumulator holds one query and four
 //   consecutive keys, so the row maximum is an in-lane max plus two lane
@@ -55,6 +60,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per work-group
 constexpr int kBN = 64;           // keys per tile
 constexpr float kRebase = 8.f;    // lazy rebasing threshold (log2 units)
+
+// Causal balance: 1 = one work-group per (heavy, light) query-tile pair;
+// 0 = one work-group per query tile, heaviest tile of each (batch, head)
+// first.  Pairing halves the work-groups per head, so the 64 work-groups an
+// XCD holds at once span twice as many heads and their K/V (2 MiB per head
+// at 4096 keys) no longer fits the XCD's 4 MiB L2: measured HBM traffic rose
+// from 1.0x to 1.7x the algorithmic bytes for 3% more speed.  Off by default.
+#ifndef FA_FAST_PAIR
+#define FA_FAST_PAIR 0
+#endif
 
 // Pace LDS operand reads against the MFMAs that consume them (bounds the
 // registers held by fragments in flight).
@@ -92,8 +107,20 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Swizzle of the 16-byte chunk index inside a row of an LDS tile (depends on
+// row % 16 only).  D = 128 (256-byte rows): a permutation of 0..15 over 16
+// rows whose upper three bits are distinct over any 8 consecutive rows.
+// D = 64 (128-byte rows, two rows per 256 bytes): together with the row
+// parity it separates 16 rows, and its upper two bits separate the rows of
+// equal parity among any 8 consecutive rows.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
 // Tile of kBN rows x D bf16 in LDS: R 16-byte chunks per row, chunk c of row
-// r at chunk position c ^ (r & 7).
+// r at chunk position c ^ swz<D>(r).
 template <int D>
 struct SwzTile {
   static constexpr int R = D / 8;
@@ -106,36 +133,32 @@ struct SwzTile {
 // Per-lane parts of every address the kernel forms.
 template <int DK, int DV>
 struct LaneAddr {
-  int k[2];                   // K fragment base, k-step parity t & 1
-  int v[4];                   // V^T transposed-read base, dim block db & 3
+  int k[DK / 32];             // K fragment base per k-step
+  int v[DV / 16];             // V^T transposed-read base per 16-dim block
   int kld[SwzTile<DK>::IPW];  // element offset (row * DK + chunk * 8) of each direct K load
   int vld[SwzTile<DV>::IPW];
 
   __device__ __forceinline__ void init(int lane, int wave) {
     const int r16 = lane & 15, g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
-    // K fragment (key block kb, k-step t): row 16kb + r16, chunk 4t + g; with
-    // x = r16 & 7 the swizzled chunk is 8(t/2) + ((g ^ x) ^ 4(t & 1)).
-    const int x = r16 & 7;
-    k[0] = r16 * SwzTile<DK>::ROW + 16 * (g ^ x);
-    k[1] = r16 * SwzTile<DK>::ROW + 16 * ((g ^ x) ^ 4);
-    // V^T read (dim block db, key row 32kt + 16h + 4g + e, bytes 8(r & 1)
-    // of chunk 2db + r/2): with z = (4g + e) & 7 the swizzled chunk is
-    // 8(db / 4) + ((2(db % 4) + r/2) ^ z).
-    const int z = (4 * g + e) & 7;
+    // K fragment (key block kb, k-step t): row 16kb + r16, chunk 4t + g
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      v[b] = (4 * g + e) * SwzTile<DV>::ROW + 16 * ((2 * b + (r >> 1)) ^ z) + 8 * (r & 1);
+    for (int t = 0; t < DK / 32; ++t) k[t] = r16 * SwzTile<DK>::ROW + 16 * ((4 * t + g) ^ swz<DK>(r16));
+    // V^T read (dim block db, key row 32kt + 16h + 4g + e, bytes 8(r & 1) of
+    // chunk 2db + r/2); 32kt + 16h leaves row % 16 and so the swizzle alone
+#pragma unroll
+    for (int db = 0; db < DV / 16; ++db)
+      v[db] = (4 * g + e) * SwzTile<DV>::ROW + 16 * ((2 * db + (r >> 1)) ^ swz<DV>(4 * g + e)) + 8 * (r & 1);
 #pragma unroll
     for (int i = 0; i < SwzTile<DK>::IPW; ++i) {
       const int slot = (wave * SwzTile<DK>::IPW + i) * 64 + lane;
       const int row = slot / SwzTile<DK>::R;
-      kld[i] = row * DK + ((slot % SwzTile<DK>::R) ^ (row & 7)) * 8;
+      kld[i] = row * DK + ((slot % SwzTile<DK>::R) ^ swz<DK>(row)) * 8;
     }
 #pragma unroll
     for (int i = 0; i < SwzTile<DV>::IPW; ++i) {
       const int slot = (wave * SwzTile<DV>::IPW + i) * 64 + lane;
       const int row = slot / SwzTile<DV>::R;
-      vld[i] = row * DV + ((slot % SwzTile<DV>::R) ^ (row & 7)) * 8;
+      vld[i] = row * DV + ((slot % SwzTile<DV>::R) ^ swz<DV>(row)) * 8;
     }
   }
 };
@@ -147,14 +170,18 @@ struct LaneAddr {
 template <int D, int IPW>
 __device__ __forceinline__ void load_tile(const uint16_t* tile, int rows_left, const int (&ld)[IPW], lds_char* dst,
                                           int wave) {
+  if (rows_left >= kBN) {
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    int off = ld[i];
-    if (rows_left < kBN) {
-      const int row = off / D;
-      if (row >= rows_left) off += (rows_left - 1 - row) * D;
+    for (int i = 0; i < IPW; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(tile + ld[i]), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0,
+                                       0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = ld[i] / D;
+      const int off = ld[i] + (min(row, rows_left - 1) - row) * D;
+      __builtin_amdgcn_global_load_lds((gbl_void*)(tile + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((gbl_void*)(tile + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
   }
 }
 
@@ -174,9 +201,14 @@ __device__ __forceinline__ void qk_tile(f32x4 (&s)[4][2], const QFrag<DK>& q, co
   for (int kb = 0; kb < 4; ++kb) {
     s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // k-step outermost: consecutive MFMAs feed eight different accumulators,
+  // so none waits on the result of the one issued just before it
 #pragma unroll
-    for (int t = 0; t < DK / 32; ++t) {
-      const bf16x8 a = *(const lds_bf16x8*)(kt + la.k[t & 1] + 16 * kb * ROW + 128 * (t >> 1));
+  for (int t = 0; t < DK / 32; ++t) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 a = *(const lds_bf16x8*)(kt + la.k[t] + 16 * kb * ROW);
       s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.f[0][t], s[kb][0], 0, 0, 0);
       s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.f[1][t], s[kb][1], 0, 0, 0);
     }
@@ -203,11 +235,12 @@ template <int DK, int DV>
 __device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&pb)[2][2], const lds_char* vt,
                                         const LaneAddr<DK, DV>& la) {
   constexpr int ROW = SwzTile<DV>::ROW;
+  // k-step outermost: consecutive MFMAs feed different accumulators
 #pragma unroll
-  for (int db = 0; db < DV / 16; ++db) {
+  for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const lds_char* p = vt + la.v[db & 3] + 32 * kt * ROW + 128 * (db >> 2);
+    for (int db = 0; db < DV / 16; ++db) {
+      const lds_char* p = vt + la.v[db] + 32 * kt * ROW;
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * ROW));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -367,9 +400,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, causal != 0);
+  // Under a causal mask query tile i visits about i + 1 key tiles; a
+  // work-group takes the pair (n_qt - 1 - u, u), heavy one first, so that
+  // every work-group does the same work and the grid drains evenly.
+  const bool pair = causal != 0 && FA_FAST_PAIR;
+  const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, causal != 0 && !pair);
+  const int n_pass = (pair && 2 * tc.qt + 1 != n_qt) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qt = pair ? (pass == 0 ? n_qt - 1 - tc.qt : tc.qt) : tc.qt;
   const int b = tc.bh / H;
-  const int q0 = tc.qt * kBM;
+  const int q0 = qt * kBM;
   const int klen = clamp_klen(k_len, b, Nk);
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
@@ -467,12 +508,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     if (lse != nullptr && g == 0)
       lse[bh * Nq + qrow[qb]] = nonempty ? (ft.st.m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
+  }  // pass
 }
 
 template <int DK, int DV, bool BIAS>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
-  const long long total = (long long)n_qt * a.H * a.B;
+  const int n_units = (a.causal && FA_FAST_PAIR) ? (n_qt + 1) / 2 : n_qt;
+  const long long total = (long long)n_units * a.H * a.B;
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & 15) == 0);
   hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
