@@ -25,17 +25,22 @@ Modules:
 * ``online`` -- the pages' tile recurrence with arbitrary key partitions and
   visiting orders, plus the two-block merge; used to pin the recurrence
   itself (tile-size and order invariance, the printed chunk states).
+* ``backward`` -- gradients by recomputation from the saved output and
+  log-sum-exp ([GS] section 7; [VW] Step 8).
 
 Parity pins: every function here is pinned by ``-m "not gpu"`` tests against
 the pages' printed worked examples, closed forms, invariants and an
 independent library routine; no function is "parity unpinned".
 """
 
+from .backward import attention_bwd_head, attention_bwd_ref
 from .dense import allowed_mask, attention_head, attention_ref
 from .online import block_state, even_tiles, merge_states, online_ref
 
 __all__ = [
     "allowed_mask",
+    "attention_bwd_head",
+    "attention_bwd_ref",
     "attention_head",
     "attention_ref",
     "block_state",

@@ -18,7 +18,11 @@ What pins the oracle (none of it is the oracle's own formula retyped):
   visiting order;
 * an independent library routine: torch's CPU scaled_dot_product_attention
   in float64 under an explicit additive mask (rows with at least one allowed
-  key), and scipy's logsumexp for lse.
+  key), and scipy's logsumexp for lse;
+* for the backward ([GS] section 7): torch autograd of the plain operator in
+  float64, central finite differences of the forward definition, and the
+  identities the recomputed gradients satisfy (identical keys, row sums of P
+  and of D, empty rows, a single visible key).
 """
 
 import itertools
@@ -530,6 +534,140 @@ def pin_sampled_rows(orc):
         _close(lz[n], math.log(cnt), 1e-13, f"sampled equal-logit lse row {i}")
 
 
+# --------------------------------------------------------------------------
+# backward by recomputation ([GS] section 7, [VW] Step 8)
+# --------------------------------------------------------------------------
+
+def _bwd_case(rng, bsz, heads, nq, nk, dk, dv, scale_g=1.0):
+    q = rng.standard_normal((bsz, heads, nq, dk))
+    k = rng.standard_normal((bsz, heads, nk, dk))
+    v = rng.standard_normal((bsz, heads, nk, dv))
+    g = rng.standard_normal((bsz, heads, nq, dv)) * scale_g
+    return q, k, v, g
+
+
+def pin_bwd_autograd(orc):
+    """torch autograd (float64, CPU) of the plain operator gives the same
+    dQ, dK, dV: an independent differentiation of the definition.  Only rows
+    with an allowed key enter the autograd graph (softmax over an empty set
+    has no derivative); the oracle must give those rows' dQ = 0."""
+    import torch
+
+    rng = np.random.default_rng(41)
+    for (bsz, heads, nq, nk, dk, dv, causal, k_len, use_bias, scale) in (
+            (2, 2, 7, 9, 5, 3, True, [9, 6], True, 0.37),
+            (1, 2, 9, 4, 2, 6, False, [3], False, 1.0),
+            (2, 1, 5, 12, 8, 8, True, [12, 0], True, 1.0 / math.sqrt(8)),
+            (1, 1, 12, 5, 3, 4, True, None, False, 0.9),   # Nq > Nk: empty top rows
+    ):
+        q, k, v, g = _bwd_case(rng, bsz, heads, nq, nk, dk, dv)
+        bias = rng.standard_normal((bsz, heads, nq, nk)) if use_bias else None
+        dq, dk_, dv_ = orc.attention_bwd_ref(q, k, v, g, scale=scale, causal=causal, k_len=k_len, bias=bias)
+        for b in range(bsz):
+            lim = nk if k_len is None else min(max(k_len[b], 0), nk)
+            for h in range(heads):
+                rows = [i for i in range(nq) if (min(lim, i + nk - nq + 1) if causal else lim) > 0]
+                if not rows:  # every row empty: nothing depends on Q, K or V
+                    assert np.all(dq[b, h] == 0.0) and np.all(dk_[b, h] == 0.0) and np.all(dv_[b, h] == 0.0)
+                    continue
+                tq = torch.from_numpy(q[b, h]).clone().requires_grad_(True)
+                tk = torch.from_numpy(k[b, h]).clone().requires_grad_(True)
+                tv = torch.from_numpy(v[b, h]).clone().requires_grad_(True)
+                loss = torch.zeros((), dtype=torch.float64)
+                for i in rows:
+                    cnt = min(lim, i + nk - nq + 1) if causal else lim
+                    logit = (tk[:cnt] @ tq[i]) * scale
+                    if bias is not None:
+                        logit = logit + torch.from_numpy(bias[b, h, i, :cnt])
+                    o_i = torch.softmax(logit, dim=0) @ tv[:cnt]
+                    loss = loss + (o_i * torch.from_numpy(g[b, h, i])).sum()
+                gq, gk, gv = torch.autograd.grad(loss, (tq, tk, tv), allow_unused=False)
+                _close(dq[b, h], gq.numpy(), 1e-12, "dQ vs autograd")
+                _close(dk_[b, h], gk.numpy(), 1e-12, "dK vs autograd")
+                _close(dv_[b, h], gv.numpy(), 1e-12, "dV vs autograd")
+                empty = [i for i in range(nq) if i not in rows]
+                assert np.all(dq[b, h, empty] == 0.0), "empty rows must give dQ = 0"
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of the loss sum(G * O), O from the oracle's
+    forward definition, match the backward on a tiny masked, biased case."""
+    rng = np.random.default_rng(43)
+    nq, nk, dk, dv, scale = 4, 5, 3, 2, 0.7
+    q, k, v, g = _bwd_case(rng, 1, 1, nq, nk, dk, dv)
+    bias = rng.standard_normal((1, 1, nq, nk))
+    kw = dict(scale=scale, causal=True, k_len=[4], bias=bias)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attention_ref(qq, kk, vv, **kw)
+        return float(np.sum(o * g))
+
+    dq, dk_, dv_ = orc.attention_bwd_ref(q, k, v, g, **kw)
+    eps = 1e-6
+    for x, gx, name in ((q, dq, "dQ"), (k, dk_, "dK"), (v, dv_, "dV")):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        _close(gx, num, 1e-7, f"{name} vs central differences")
+
+
+def pin_bwd_invariants(orc):
+    """Identities of the recomputed gradients: with identical keys dQ = 0;
+    each non-empty row's probabilities sum to one, so the keys' dV sum to the
+    sum of the non-empty rows' G; each row of D sums to zero, so the keys'
+    dK sum to zero; an empty row contributes nothing; passing the forward's
+    O and lse explicitly changes nothing."""
+    rng = np.random.default_rng(47)
+    nq, nk, dk, dv = 6, 7, 4, 3
+    q, k, v, g = _bwd_case(rng, 1, 1, nq, nk, dk, dv)
+    kk = np.repeat(k[:, :, :1], nk, axis=2)
+    dq, _, _ = orc.attention_bwd_ref(q, kk, v, g, scale=0.8, causal=True)
+    _close(dq, np.zeros_like(dq), 1e-13, "identical keys give dQ = 0")
+    bias = rng.standard_normal((1, 1, nq, nk))
+    for k_len in ([7], [3], [0]):
+        dq, dk_, dv_ = orc.attention_bwd_ref(q, k, v, g, scale=0.8, causal=True, k_len=k_len, bias=bias)
+        ok = orc.allowed_mask(np.arange(nq), nq, nk, True, k_len[0])
+        rows = ok.any(axis=1)
+        _close(dv_[0, 0].sum(axis=0), g[0, 0, rows].sum(axis=0), 1e-12, "sum_j dV_j = sum of G")
+        _close(dk_[0, 0].sum(axis=0), np.zeros(dk), 1e-12, "sum_j dK_j = 0")
+        assert np.all(dq[0, 0, ~rows] == 0.0)
+        assert np.all(dk_[0, 0, k_len[0]:] == 0.0) and np.all(dv_[0, 0, k_len[0]:] == 0.0), \
+            "keys past k_len get no gradient"
+        o, lse = orc.attention_ref(q, k, v, scale=0.8, causal=True, k_len=k_len, bias=bias)
+        e = orc.attention_bwd_ref(q, k, v, g, scale=0.8, causal=True, k_len=k_len, bias=bias, o=o, lse=lse)
+        for a, b_ in zip(e, (dq, dk_, dv_)):
+            _close(a, b_, 1e-14, "explicit O and lse")
+    # an extra empty row (Nq > Nk under bottom-right causal) with any G
+    q2 = np.concatenate([rng.standard_normal((1, 1, 1, dk)), q], axis=2)
+    g2 = np.concatenate([rng.standard_normal((1, 1, 1, dv)) * 100, g], axis=2)
+    k2, v2 = k[:, :, :nq], v[:, :, :nq]
+    a = orc.attention_bwd_ref(q[:, :, :], k2, v2, g, scale=0.8, causal=True)
+    b_ = orc.attention_bwd_ref(q2, k2, v2, g2, scale=0.8, causal=True)
+    _close(b_[1], a[1], 1e-13, "empty row leaves dK unchanged")
+    _close(b_[2], a[2], 1e-13, "empty row leaves dV unchanged")
+    assert np.all(b_[0][0, 0, 0] == 0.0)
+
+
+def pin_bwd_single_key(orc):
+    """Closed form: a row that sees one key has p = 1 and o = v, so its D row
+    is zero (dQ_i = 0) and it passes g_i straight to that key's dV; with a
+    1x1 problem dK = 0 and dV = g."""
+    rng = np.random.default_rng(53)
+    q, k, v, g = _bwd_case(rng, 1, 1, 1, 1, 3, 2)
+    dq, dk_, dv_ = orc.attention_bwd_ref(q, k, v, g, scale=1.3)
+    _close(dq, np.zeros_like(dq), 1e-15, "1x1 dQ")
+    _close(dk_, np.zeros_like(dk_), 1e-15, "1x1 dK")
+    _close(dv_, g, 1e-15, "1x1 dV")
+    q, k, v, g = _bwd_case(rng, 1, 1, 4, 4, 3, 2)
+    dq, _, dv_ = orc.attention_bwd_ref(q, k, v, g, scale=1.3, causal=True)
+    _close(dq[0, 0, 0], np.zeros(3), 1e-15, "row 0 under causal sees key 0 only")
+
+
 PINS = [
     pin_gs_sec2_tile_local_counterexample,
     pin_gs_sec4_rescale_both,
@@ -546,6 +684,10 @@ PINS = [
     pin_tile_size_invariance,
     pin_library_sdpa,
     pin_sampled_rows,
+    pin_bwd_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_invariants,
+    pin_bwd_single_key,
 ]
 
 

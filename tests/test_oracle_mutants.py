@@ -103,6 +103,33 @@ MUTANTS = [
      "e = np.exp(x - m)\n    return m, e.sum(), e @ vals", "e = np.exp(x)\n    return m, e.sum(), e @ vals"),
     ("block_state_normalised", "online.py",
      "return m, e.sum(), e @ vals", "return m, e.sum(), (e @ vals) / e.sum()"),
+    # --- backward by recomputation ------------------------------------------
+    ("bwd_c_dropped", "backward.py",
+     "d = p * (g @ v.T - c[:, None])", "d = p * (g @ v.T)"),
+    ("bwd_c_sign", "backward.py",
+     "d = p * (g @ v.T - c[:, None])", "d = p * (g @ v.T + c[:, None])"),
+    ("bwd_c_from_v", "backward.py",
+     "c = np.sum(g * o, axis=1)", "c = np.sum(g, axis=1) * 0.5"),
+    ("bwd_dq_unscaled", "backward.py",
+     "dq = float(scale) * (d @ k)", "dq = (d @ k)"),
+    ("bwd_dk_unscaled", "backward.py",
+     "dk = float(scale) * (d.T @ q)", "dk = (d.T @ q)"),
+    ("bwd_dk_uses_p", "backward.py",
+     "dk = float(scale) * (d.T @ q)", "dk = float(scale) * (p.T @ q)"),
+    ("bwd_dq_uses_v", "backward.py",
+     "dq = float(scale) * (d @ k)", "dq = float(scale) * (d @ v[:, :1].repeat(k.shape[1], axis=1))"),
+    ("bwd_dv_uses_d", "backward.py",
+     "dv = p.T @ g", "dv = d.T @ g"),
+    ("bwd_dv_rows_reversed", "backward.py",
+     "dv = p.T @ g", "dv = p.T @ g[::-1]"),
+    ("bwd_lse_sign", "backward.py",
+     "np.exp(np.where(ok, s, 0.0) - lse_safe[:, None])", "np.exp(np.where(ok, s, 0.0) + lse_safe[:, None])"),
+    ("bwd_mask_ignored", "backward.py",
+     "p = np.where(ok & nonempty[:, None],", "p = np.where(nonempty[:, None] | True,"),
+    ("bwd_bias_ignored", "backward.py",
+     "s = s + np.asarray(bias, dtype=np.float64)", "s = s"),
+    ("bwd_scale_dropped_in_logits", "backward.py",
+     "s = (q @ k.T) * float(scale)", "s = (q @ k.T)"),
 ]
 
 
