@@ -58,7 +58,7 @@ typedef enum {
                              or too large for 32-bit grid/index arithmetic   */
   FA_ERR_UNSUPPORTED = 3, /* dtype, head dim (> 128), block_n, chunk, causal
                              flag or scale outside what the kernels support  */
-  FA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small          */
+  FA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small     */
   FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
 } fa_status;
 
@@ -134,6 +134,52 @@ int fa_check_decode(const void* q, const void* k_cache, const void* v_cache,
                     int B, int H, int Nk_max, int dk, int dv, int chunk,
                     int dtype, float scale, const void* workspace,
                     size_t workspace_bytes);
+
+/*
+ * Bytes of fp32 workspace fa_bwd needs: B * H * Nq * 4 (one scalar per query
+ * row).  Returns 0 for negative sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+
+/*
+ * fa_bwd -- gradients of fa_fwd by recomputation ([GS] section 7, "Why
+ * training need not save the full probability matrix"; [VW] Step 8).  The
+ * forward's O and lse are consumed; the probabilities are rebuilt tile by
+ * tile from Q, K, the same masks and the same bias, and never stored:
+ *
+ *   p_ij = exp(s_ij - lse_i) on the allowed set (0 elsewhere)
+ *   c_i  = dO_i . O_i,   D_ij = p_ij (dO_i . v_j - c_i)
+ *   dV = P^T dO,   dQ = scale * D K,   dK = scale * D^T Q
+ *
+ *   q, k, v    as for fa_fwd                           read only
+ *   o          [B, H, Nq, dv] dtype: fa_fwd's output    read only
+ *   dout       [B, H, Nq, dv] dtype: dLoss/dO           read only
+ *   lse        [B, H, Nq] fp32: fa_fwd's lse, required  read only
+ *   bias, k_len, scale, causal: exactly as passed to fa_fwd (the bias is a
+ *              fixed input: no bias gradient is formed)
+ *   dq [B, H, Nq, dk], dk [B, H, Nk, dk], dv [B, H, Nk, dv]  dtype,
+ *              written in full (keys no row can see get zero)
+ *   workspace: device buffer of at least fa_bwd_workspace_bytes(B, H, Nq)
+ *              bytes, 16-byte aligned; contents on entry are ignored.
+ *   1 <= dk, dv <= 128; B * H <= 65535.  Rows whose lse is -inf (no allowed
+ *   key) contribute nothing.  Launches (all on `stream`, no atomics, results
+ *   bitwise reproducible): c per row, then dK/dV per key tile, then dQ per
+ *   query tile.  Inputs must be finite; lse must be the forward's (a
+ *   different lse rescales the rebuilt probabilities).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, const float* bias,
+           const int32_t* k_len, void* dq, void* dk, void* dv, int B, int H,
+           int Nq, int Nk, int d_k, int d_v, int dtype, float scale,
+           int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only validation of fa_bwd's arguments. */
+int fa_check_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, const float* bias,
+                 const int32_t* k_len, const void* dq, const void* dk,
+                 const void* dv, int B, int H, int Nq, int Nk, int d_k,
+                 int d_v, int dtype, float scale, int causal,
+                 const void* workspace, size_t workspace_bytes);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(int status);

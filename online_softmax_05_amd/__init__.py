@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FaError", "lib", "lib_path",
     "fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
-    "fa_check_fwd", "fa_check_decode", "fa_status_str", "fa_abi_version",
+    "fa_check_fwd", "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
+    "fa_status_str", "fa_abi_version",
 ]
 
 FA_F32 = 0
@@ -44,6 +45,11 @@ _SIGNATURES = {
     "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
+    "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _ip, _vp, _vp, _vp,
+                    _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "fa_check_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _ip, _vp, _vp, _vp,
+                          _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
 }
@@ -221,3 +227,62 @@ def fa_decode_splitk(q, k_cache, v_cache, k_len, *, scale=None, chunk=512, out=N
     if st != 0:
         raise FaError(st)
     return out, lse
+
+
+def fa_bwd_workspace_bytes(B, H, Nq):
+    return lib().fa_bwd_workspace_bytes(B, H, Nq)
+
+
+def fa_check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale,
+                 causal, workspace, workspace_bytes):
+    """Host-only validation (integer addresses; nothing is dereferenced)."""
+    return lib().fa_check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype,
+                              float(scale), causal, workspace, workspace_bytes)
+
+
+def fa_bwd(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=False, dq=None, dk=None,
+           dv=None, workspace=None):
+    """Gradients of fa_fwd by recomputation from its output ``o`` and ``lse``:
+    q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv], o and dout [B,H,Nq,dv],
+    lse fp32 [B,H,Nq]; bias, k_len, scale and causal as given to fa_fwd.
+    Returns (dq, dk, dv) in the input dtype."""
+    _need(q, "q", dims=4)
+    dev = q.device
+    _need(k, "k", dtype=q.dtype, dims=4, device=dev)
+    _need(v, "v", dtype=q.dtype, dims=4, device=dev)
+    _need(o, "o", dtype=q.dtype, dims=4, device=dev)
+    _need(dout, "dout", dtype=q.dtype, dims=4, device=dev)
+    _need(lse, "lse", dtype=torch.float32, dims=3, device=dev)
+    B, H, Nq, d_k = q.shape
+    Nk, d_v = k.shape[2], v.shape[3]
+    if (tuple(k.shape) != (B, H, Nk, d_k) or tuple(v.shape) != (B, H, Nk, d_v)
+            or tuple(o.shape) != (B, H, Nq, d_v) or tuple(dout.shape) != (B, H, Nq, d_v)
+            or tuple(lse.shape) != (B, H, Nq)):
+        raise FaError(2, "q/k/v/o/dout/lse shapes do not match")
+    if bias is not None:
+        _need(bias, "bias", dtype=torch.float32, dims=4, device=dev)
+        if tuple(bias.shape) != (B, H, Nq, Nk):
+            raise FaError(2, "bias must be [B,H,Nq,Nk]")
+    if k_len is not None:
+        _need(k_len, "k_len", dtype=torch.int32, dims=1, device=dev)
+        if k_len.shape[0] != B:
+            raise FaError(2, f"k_len must have {B} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    need = fa_bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    else:
+        _need(workspace, "workspace", dtype=torch.float32, dims=1, device=dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(bias), _ptr(k_len),
+                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d_k, d_v, _dtype_code(q), float(scale),
+                      int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(dev))
+    if st != 0:
+        raise FaError(st)
+    return dq, dk, dv

@@ -77,11 +77,39 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* k_l
   return FA_OK;
 }
 
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              const float* bias, const int32_t* k_len, const void* dq, const void* dk, const void* dv, int B, int H,
+              int Nq, int Nk, int d_k, int d_v, int dtype, float scale, int causal, const void* workspace,
+              size_t workspace_bytes) {
+  (void)bias;
+  (void)k_len;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (d_k < 1 || d_v < 1) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d_k > kMaxHeadDim || d_v > kMaxHeadDim) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  // grids are (row or key tiles, B*H): the second grid dimension is 16-bit
+  if (!product_fits({B, H}, 65535)) return FA_ERR_SHAPE;
+  if (Nq > kInt32Max - Nk) return FA_ERR_SHAPE;
+  const long long bhq = (long long)B * H * Nq, bhk = (long long)B * H * Nk;
+  if (bhq == 0 && bhk == 0) return FA_OK;  // nothing to compute
+  if (bhk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return FA_ERR_NULL;
+  if (bhq > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
+    return FA_ERR_NULL;
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return FA_ERR_WORKSPACE;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fa_abi_version(void) { return 100; }
+int fa_abi_version(void) { return 101; }
 
 const char* fa_status_str(int status) {
   switch (status) {
@@ -89,7 +117,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large shape";
     case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block_n, chunk, causal flag or scale";
-    case FA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -143,6 +171,34 @@ int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache, co
                    ws, ws == nullptr ? nullptr : ws + (size_t)B * H * max_chunks * dv, max_chunks};
   const hipError_t e = dtype == FA_BF16 ? fa::launch_decode_bf16(a, static_cast<hipStream_t>(stream))
                                         : fa::launch_decode_f32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 0 || H < 0 || Nq < 0) return 0;
+  return (size_t)B * H * Nq * sizeof(float);
+}
+
+int fa_check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 const float* bias, const int32_t* k_len, const void* dq, const void* dk, const void* dv, int B, int H,
+                 int Nq, int Nk, int d_k, int d_v, int dtype, float scale, int causal, const void* workspace,
+                 size_t workspace_bytes) {
+  return check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale, causal,
+                   workspace, workspace_bytes);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           const float* bias, const int32_t* k_len, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+           int d_k, int d_v, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  const int st = check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale,
+                           causal, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0 && (long long)B * H * Nk == 0) return FA_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fa::BwdArgs a{q,  k,  v,  o,  dout, lse, bias, k_len, dq,  dk,  dv,
+                static_cast<float*>(workspace), B, H, Nq, Nk, d_k, d_v, scale, causal};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_general_bf16(a, s) : fa::launch_bwd_general_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

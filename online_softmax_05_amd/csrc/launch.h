@@ -35,6 +35,24 @@ struct DecodeArgs {
   int max_chunks;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;  // upstream gradient dLoss/dO
+  const float* lse;
+  const float* bias;
+  const int32_t* k_len;
+  void* dq_out;
+  void* dk_out;
+  void* dv_out;
+  float* ws_c;  // [B*H*Nq]: c_i = dO_i . O_i
+  int B, H, Nq, Nk, dk, dv;
+  float scale;
+  int causal;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // fast bf16 path: head dims 64/128, 16-byte aligned tensors, 64-key tiles
@@ -43,5 +61,7 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_bwd_general_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_general_bf16(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

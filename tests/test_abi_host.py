@@ -33,7 +33,8 @@ def test_library_built():
 def test_exports_every_declared_symbol():
     names = header_functions()
     assert {"fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes", "fa_check_fwd",
-            "fa_check_decode", "fa_status_str", "fa_abi_version"} <= set(names)
+            "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd", "fa_status_str",
+            "fa_abi_version"} <= set(names)
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
@@ -58,7 +59,7 @@ def test_header_is_plain_c():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 100
+    assert fa.fa_abi_version() == 101
     for st in range(6):
         assert isinstance(fa.fa_status_str(st), str) and fa.fa_status_str(st)
     assert fa.fa_status_str(0) == "ok"
@@ -151,6 +152,40 @@ def check_dec(**kw):
 ])
 def test_check_decode(kw, want):
     assert check_dec(**kw) == want
+
+
+def check_bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, bias=None, k_len=None, dq=P, dk=P, dv=P, B=2, H=3, Nq=100,
+             Nk=120, d_k=64, d_v=32, dtype=fa.FA_BF16, scale=0.125, causal=1, ws=P, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = fa.fa_bwd_workspace_bytes(a["B"], a["H"], a["Nq"])
+    return fa.fa_check_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["bias"], a["k_len"],
+                           a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d_k"], a["d_v"],
+                           a["dtype"], a["scale"], a["causal"], a["ws"], a["ws_bytes"])
+
+
+def test_bwd_workspace_bytes():
+    f = fa.fa_bwd_workspace_bytes
+    assert f(2, 3, 100) == 2 * 3 * 100 * 4
+    assert f(0, 3, 100) == 0 and f(-1, 3, 100) == 0 and f(1, 1, -5) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, OK), ({"dtype": fa.FA_F32}, OK), ({"bias": P, "k_len": P}, OK), ({"causal": 0}, OK),
+    ({"lse": None}, NULL), ({"q": None}, NULL), ({"o": None}, NULL), ({"dout": None}, NULL),
+    ({"dq": None}, NULL), ({"dk": None}, NULL), ({"dv": None}, NULL), ({"k": None}, NULL), ({"v": None}, NULL),
+    ({"ws": None}, WS), ({"ws_bytes": 100}, WS), ({"ws": P + 4}, WS),
+    ({"d_k": 129}, UNSUP), ({"d_v": 0}, SHAPE), ({"B": -1}, SHAPE), ({"Nk": -1}, SHAPE), ({"Nq": -3}, SHAPE),
+    ({"causal": 2}, UNSUP), ({"scale": math.inf}, UNSUP), ({"dtype": 3}, UNSUP),
+    ({"B": 256, "H": 256}, SHAPE),                                   # B*H beyond the 16-bit grid axis
+    ({"Nq": 0, "q": None, "o": None, "dout": None, "lse": None, "dq": None, "ws": None, "ws_bytes": 0}, OK),
+    ({"Nk": 0, "k": None, "v": None, "dk": None, "dv": None}, OK),
+    ({"B": 0, "q": None, "k": None, "v": None, "o": None, "dout": None, "lse": None, "dq": None, "dk": None,
+      "dv": None, "ws": None, "ws_bytes": 0}, OK),
+])
+def test_check_bwd(kw, want):
+    assert check_bwd(**kw) == want
 
 
 def test_binding_fails_loudly_without_a_device():

@@ -137,6 +137,13 @@ def to_device(inputs, device):
     return out
 
 
+def seeded_upstream(seed, B, H, Nq, dv, dtype):
+    """A seeded upstream gradient dLoss/dO ~ N(0, 1) of shape [B,H,Nq,dv] (CPU),
+    from its own generator (seed 200 + seed)."""
+    g = torch.Generator().manual_seed(200 + seed)
+    return _randn_cpu(g, (B, H, Nq, dv)).to(dtype)
+
+
 def seeded_case(seed, B, H, Nq, Nk, dk, dv, dtype, *, causal=False, bias=False, k_len=None, q_std=1.0,
                 k_std=1.0):
     """A small seeded case of arbitrary shape (CPU), for parity sweeps.
