@@ -198,7 +198,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const hipStream_t s = static_cast<hipStream_t>(stream);
   fa::BwdArgs a{q,  k,  v,  o,  dout, lse, bias, k_len, dq,  dk,  dv,
                 static_cast<float*>(workspace), B, H, Nq, Nk, d_k, d_v, scale, causal};
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_general_bf16(a, s) : fa::launch_bwd_general_f32(a, s);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -21,8 +21,9 @@
 // atomics): c per row; dK and dV per key tile looping over query rows; dQ
 // per query tile looping over key tiles.
 //
-// This file holds the general kernels: fp32 arithmetic for fp32 and bf16
-// inputs, any head dims 1..128, LDS-staged tiles.
+// This file holds c and the general kernels: fp32 arithmetic for fp32 and
+// bf16 inputs, any head dims 1..128, LDS-staged tiles.  bf16 inputs with head
+// dims 64/128 take the matrix-core kernels of fa_bwd_bf16.hip.
 #include "fa_common.h"
 #include "launch.h"
 
@@ -243,12 +244,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_general_kernel(
 }
 
 template <typename T>
-hipError_t launch_general(const BwdArgs& a, hipStream_t stream) {
+void launch_dot(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.Nq;
-  const unsigned bh = (unsigned)(a.B * a.H);
   if (rows > 0)
     hipLaunchKernelGGL(bwd_dot_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, stream,
                        (const T*)a.dout, (const T*)a.o, a.ws_c, rows, a.dv);
+}
+
+template <typename T>
+hipError_t launch_general(const BwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.H * a.Nq;
+  const unsigned bh = (unsigned)(a.B * a.H);
+  launch_dot<T>(a, stream);
   const size_t smem = GenTiles::bytes(a.dk, a.dv);
   if (a.Nk > 0)  // with no query rows this writes dK = dV = 0
     hipLaunchKernelGGL(bwd_dkdv_general_kernel<T>, dim3((unsigned)((a.Nk + kKeys - 1) / kKeys), bh), dim3(kThreads),
@@ -263,7 +270,12 @@ hipError_t launch_general(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_general_f32(const BwdArgs& a, hipStream_t s) { return launch_general<float>(a, s); }
-hipError_t launch_bwd_general_bf16(const BwdArgs& a, hipStream_t s) { return launch_general<uint16_t>(a, s); }
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s) { return launch_general<float>(a, s); }
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+  if (!bwd_bf16_mfma_eligible(a)) return launch_general<uint16_t>(a, s);
+  launch_dot<uint16_t>(a, s);
+  return launch_bwd_bf16_mfma(a, s);
+}
 
 }  // namespace fa

@@ -1,0 +1,459 @@
+// Attention backward by recomputation on the matrix cores: bf16 inputs, head
+// dims 64 or 128 ([GS] section 7, "Why training need not save the full
+// probability matrix"; [VW] Step 8, "Backward pass: the recompute trade").
+//
+// Sources, cited by title and section:
+//   [GS] "How Does FlashAttention Preserve Global Softmax Across Tiles?"
+//   [VW] "Flash attention and efficient attention: Visual walkthrough"
+//
+//   p_ij = exp(s_ij - L_i) on the allowed set, 0 elsewhere,  c_i = g_i . o_i
+//   D_ij = p_ij (g_i . v_j - c_i)
+//   dV = P^T G,   dK = scale D^T Q,   dQ = scale D K
+//
+// Two kernels after the per-row c (bwd_dot_kernel, general file); neither
+// uses atomics, so the results are bitwise reproducible.
+//
+// dQ kernel: one work-group = 4 waves = 64 query rows of one (batch, head),
+// 16 rows per wave with their Q and G rows held as MFMA operands.  Key tiles
+// of 64 keys stream through LDS (direct-to-LDS loads, double buffered), and
+// per tile each wave forms
+//   S^T  = K Q^T     (v_mfma_f32_16x16x32_bf16; a lane holds 4 keys of one row)
+//   dP^T = V G^T
+//   D^T  = P^T o (dP^T - c)
+//   dQ^T += K^T D^T  (K^T read transposed from LDS with ds_read_b64_tr_b16;
+//                     D^T rounded to bf16 is directly the B operand)
+// dK/dV kernel: one work-group = 4 waves = 64 keys, 16 keys per wave with
+// their K and V rows as MFMA operands; query tiles of 64 rows (Q, G, L, c)
+// stream through LDS, and per tile each wave forms
+//   S = Q K^T, dP = G V^T, P, D  (a lane holds 4 rows of one key)
+//   dV^T += G^T P,  dK^T += Q^T D   (G^T, Q^T read transposed from LDS)
+// P and D are rounded to bf16 only as matrix-core operands; every sum is
+// fp32.
+#include "fa_common.h"
+#include "launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 64;  // rows of every LDS tile (keys or queries)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef const __attribute__((address_space(1))) void gbl_void;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS tile of kTile rows x D bf16, row-major, 16-byte chunk c of row r stored
+// at chunk position c ^ swz(r % 16): the 16 rows of an operand read land on
+// 16 distinct 16-byte bank positions (128-bit reads are served 16 lanes at a
+// time over 256 bytes of banks) and the 8 rows of a transposed read on 8
+// distinct 32-byte chunk pairs.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
+template <int D>
+struct Tile {
+  static constexpr int R = D / 8;   // 16-byte chunks per row
+  static constexpr int ROW = R * 16;
+  static constexpr int BYTES = kTile * ROW;
+  static constexpr int IPW = kTile * R / 64 / kWaves;  // 1 KiB direct loads per wave
+};
+
+// Per-lane address parts for one tile layout D.
+template <int D>
+struct TileAddr {
+  int frag[D / 32];  // operand read (tile row 16blk + r16, dims 32t + 8g .. +7): + 16 blk ROW
+  int tr[D / 16];    // transposed read of dim block db (tile rows 32kt + 16h + 4g + e): + (32kt + 16h) ROW
+  int ld[Tile<D>::IPW];
+
+  __device__ __forceinline__ void init(int lane, int wave) {
+    constexpr int ROW = Tile<D>::ROW;
+    const int r16 = lane & 15, g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) frag[t] = r16 * ROW + 16 * ((4 * t + g) ^ swz<D>(r16));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      tr[db] = (4 * g + e) * ROW + 16 * ((2 * db + (r >> 1)) ^ swz<D>(4 * g + e)) + 8 * (r & 1);
+#pragma unroll
+    for (int i = 0; i < Tile<D>::IPW; ++i) {
+      const int slot = (wave * Tile<D>::IPW + i) * 64 + lane;
+      const int row = slot / Tile<D>::R;
+      ld[i] = row * D + ((slot % Tile<D>::R) ^ swz<D>(row)) * 8;
+    }
+  }
+};
+
+// Direct-to-LDS load of this wave's share of a tile whose first row is `src`
+// (rows_left rows remain in the tensor); rows past the end re-read the last
+// row, so no lane reads out of bounds (those rows are masked).
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t* src, int rows_left, const TileAddr<D>& a, lds_char* dst,
+                                          int wave) {
+  constexpr int IPW = Tile<D>::IPW;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    int off = a.ld[i];
+    if (rows_left < kTile) {
+      const int row = off / D;
+      off += (min(row, rows_left - 1) - row) * D;
+    }
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 frag_read(const lds_char* p) { return *(const lds_bf16x8*)p; }
+
+__device__ __forceinline__ bf16x8 tr_read(const lds_char* p, int row_bytes16) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + row_bytes16));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Operand rows held in registers: row `row` of a [*, D] bf16 tensor as the
+// B operand of 16x16x32 products over D (dims 32t + 8g .. +7).
+template <int D>
+__device__ __forceinline__ void load_rows_b(bf16x8 (&f)[D / 32], const uint16_t* base, int row, bool valid, int g) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+    f[t] = valid ? *reinterpret_cast<const bf16x8*>(base + (size_t)row * D + 32 * t + 8 * g) : bf16x8{};
+}
+
+// Pack two 16x16 accumulator blocks (h = 0, 1) of fp32 values into the
+// bf16 B operand of a 16x16x32 product whose 32-long k axis is the blocks'
+// row axis: slot s of lane group g holds row 16(s/4) + 4g + s%4.
+__device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
+  u32x4 w;
+  w[0] = cvt_pk_bf16(a[0], a[1]);
+  w[1] = cvt_pk_bf16(a[2], a[3]);
+  w[2] = cvt_pk_bf16(b[0], b[1]);
+  w[3] = cvt_pk_bf16(b[2], b[3]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool BIAS>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ cvec,
+    const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dq, int H, int Nq,
+    int Nk, float scale, int causal) {
+  // one array, buffers addressed by offset (a runtime-indexed table of
+  // separate __shared__ arrays would go through a global constant table)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
+  lds_char* const kbase = (lds_char*)smem;
+  lds_char* const vbase = kbase + 2 * Tile<DK>::BYTES;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  const int q0 = blockIdx.x * kTile;
+  const int klen = clamp_klen(k_len, b, Nk);
+  const int shift = Nk - Nq;
+  const int row = q0 + 16 * wave + r16;  // this lane's query row
+  const bool rvalid = row < Nq;
+
+  TileAddr<DK> ka;
+  TileAddr<DV> va;
+  ka.init(lane, wave);
+  va.init(lane, wave);
+  const uint16_t* kbh = k + bh * Nk * DK;
+  const uint16_t* vbh = v + bh * Nk * DV;
+
+  bf16x8 qf[DK / 32], gf[DV / 32];
+  load_rows_b<DK>(qf, q + bh * Nq * DK, row, rvalid, g);
+  load_rows_b<DV>(gf, dout + bh * Nq * DV, row, rvalid, g);
+  const float l_row = rvalid ? lse[bh * Nq + row] : kNegInf;
+  const bool live = l_row != kNegInf;  // rows without an allowed key contribute nothing
+  const float l2 = live ? l_row * kLog2e : 0.f;
+  const float c_row = rvalid ? cvec[bh * Nq + row] : 0.f;
+  const float c2 = scale * kLog2e;
+  const int row_end = !live ? 0 : (causal ? min(klen, row + shift + 1) : klen);
+  const float* brow = BIAS ? bias + (bh * Nq + (size_t)(rvalid ? row : 0)) * Nk : nullptr;
+
+  f32x4 acc[DK / 16];
+#pragma unroll
+  for (int d = 0; d < DK / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kend = visible_key_end(klen, causal != 0, min(q0 + kTile, Nq) - 1, Nq, Nk);
+  const int n_tiles = kend > 0 ? (kend + kTile - 1) / kTile : 0;
+  // tiles visible in full to the work-group's first row need no mask
+  const int first_end = causal ? min(klen, q0 + shift + 1) : klen;
+  const int n_full = min(n_tiles, max(first_end, 0) / kTile);
+
+  if (n_tiles > 0) {
+    load_tile<DK>(kbh, Nk, ka, kbase, wave);
+    load_tile<DV>(vbh, Nk, va, vbase, wave);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int par = t & 1;
+    wait_loads();
+    __syncthreads();  // tile t visible; tile t-1's buffers free
+    const int j0 = t * kTile;
+    if (t + 1 < n_tiles) {
+      load_tile<DK>(kbh + (size_t)(j0 + kTile) * DK, Nk - (j0 + kTile), ka, kbase + (par ^ 1) * Tile<DK>::BYTES,
+                    wave);
+      load_tile<DV>(vbh + (size_t)(j0 + kTile) * DV, Nk - (j0 + kTile), va, vbase + (par ^ 1) * Tile<DV>::BYTES,
+                    wave);
+    }
+    const lds_char* kt = kbase + par * Tile<DK>::BYTES;
+    const lds_char* vt = vbase + par * Tile<DV>::BYTES;
+    const bool masked = t >= n_full || !live || BIAS;
+    // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of `row`
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) s[kb] = mfma(frag_read(kt + ka.frag[i] + 16 * kb * Tile<DK>::ROW), qf[i], s[kb]);
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i) dp[kb] = mfma(frag_read(vt + va.frag[i] + 16 * kb * Tile<DV>::ROW), gf[i], dp[kb]);
+    }
+    // P^T and D^T = P^T o (dP^T - c)
+    f32x4 dsv[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key0 = j0 + 16 * kb + 4 * g;
+      f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+      if (BIAS) bv = load_bias4(brow, key0, Nk, false, rvalid);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float arg = fmaf(s[kb][j], c2, -l2);
+        if (BIAS) arg = fmaf(bv[j], kLog2e, arg);
+        float p = fast_exp2(arg);
+        if (masked && key0 + j >= row_end) p = 0.f;
+        dsv[kb][j] = p * (dp[kb][j] - c_row);
+      }
+    }
+    // dQ^T += K^T D^T over the tile's two 32-key steps
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+      const bf16x8 bop = pack_b(dsv[2 * kt2], dsv[2 * kt2 + 1]);
+#pragma unroll
+      for (int db = 0; db < DK / 16; ++db)
+        acc[db] = mfma(tr_read(kt + ka.tr[db] + 32 * kt2 * Tile<DK>::ROW, 16 * Tile<DK>::ROW), bop, acc[db]);
+    }
+  }
+
+  if (rvalid) {
+    uint16_t* out = dq + (bh * Nq + row) * (size_t)DK;
+#pragma unroll
+    for (int d = 0; d < DK / 16; ++d) {
+      u32x2 w;
+      w[0] = cvt_pk_bf16(acc[d][0] * scale, acc[d][1] * scale);
+      w[1] = cvt_pk_bf16(acc[d][2] * scale, acc[d][3] * scale);
+      *reinterpret_cast<u32x2*>(out + 16 * d + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool BIAS>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ cvec,
+    const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int H, int Nq, int Nk, float scale, int causal) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
+  __shared__ float lbuf[2][kTile];  // L_i log2 e (0 for rows without a key)
+  __shared__ float cbuf[2][kTile];  // c_i
+  __shared__ int ebuf[2][kTile];    // per row: keys < end are allowed
+  lds_char* const qbase = (lds_char*)smem;
+  lds_char* const gbase = qbase + 2 * Tile<DK>::BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  const int j0 = blockIdx.x * kTile;
+  const int klen = clamp_klen(k_len, b, Nk);
+  const int shift = Nk - Nq;
+  const int key = j0 + 16 * wave + r16;  // this lane's key
+  const bool kvalid = key < Nk;
+
+  TileAddr<DK> qa;
+  TileAddr<DV> ga;
+  qa.init(lane, wave);
+  ga.init(lane, wave);
+  const uint16_t* qbh = q + bh * Nq * DK;
+  const uint16_t* gbh = dout + bh * Nq * DV;
+
+  bf16x8 kf[DK / 32], vf[DV / 32];
+  load_rows_b<DK>(kf, k + bh * Nk * DK, key, kvalid, g);
+  load_rows_b<DV>(vf, v + bh * Nk * DV, key, kvalid, g);
+  const float c2 = scale * kLog2e;
+
+  f32x4 acc_v[DV / 16], acc_k[DK / 16];
+#pragma unroll
+  for (int d = 0; d < DV / 16; ++d) acc_v[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < DK / 16; ++d) acc_k[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // query tiles whose rows can see a key of this work-group
+  const int r_lo = causal ? max(0, j0 - shift) : 0;
+  const int t0 = r_lo / kTile;
+  const int t_end = j0 < klen ? (Nq + kTile - 1) / kTile : t0;
+  const int n_tiles = max(t_end - t0, 0);
+  const int key_last = min(j0 + kTile, klen) - 1;
+
+  auto stage_rows = [&](int qt, int buf) {
+    if (tid < kTile) {
+      const int r = qt * kTile + tid;
+      const bool ok = r < Nq;
+      const float l = ok ? lse[bh * Nq + r] : kNegInf;
+      const bool live = l != kNegInf;
+      lbuf[buf][tid] = live ? l * kLog2e : 0.f;
+      cbuf[buf][tid] = ok ? cvec[bh * Nq + r] : 0.f;
+      ebuf[buf][tid] = !live ? 0 : (causal ? min(klen, r + shift + 1) : klen);
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile<DK>(qbh + (size_t)t0 * kTile * DK, Nq - t0 * kTile, qa, qbase, wave);
+    load_tile<DV>(gbh + (size_t)t0 * kTile * DV, Nq - t0 * kTile, ga, gbase, wave);
+    stage_rows(t0, 0);
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    const int qt = t0 + it;
+    const int par = it & 1;
+    wait_loads();
+    __syncthreads();
+    const int q0 = qt * kTile;
+    if (it + 1 < n_tiles) {
+      load_tile<DK>(qbh + (size_t)(q0 + kTile) * DK, Nq - (q0 + kTile), qa, qbase + (par ^ 1) * Tile<DK>::BYTES,
+                    wave);
+      load_tile<DV>(gbh + (size_t)(q0 + kTile) * DV, Nq - (q0 + kTile), ga, gbase + (par ^ 1) * Tile<DV>::BYTES,
+                    wave);
+      stage_rows(qt + 1, par ^ 1);
+    }
+    const lds_char* qt_l = qbase + par * Tile<DK>::BYTES;
+    const lds_char* gt_l = gbase + par * Tile<DV>::BYTES;
+    // no mask when every row of the tile exists and sees every key of the group
+    const bool masked = BIAS || q0 + kTile > Nq || key_last < j0 + kTile - 1 || (causal && q0 + shift < key_last);
+    // S and dP: row block rb, a lane holds rows 16rb + 4g + j of `key`
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      s[rb] = dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) s[rb] = mfma(frag_read(qt_l + qa.frag[i] + 16 * rb * Tile<DK>::ROW), kf[i], s[rb]);
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i) dp[rb] = mfma(frag_read(gt_l + ga.frag[i] + 16 * rb * Tile<DV>::ROW), vf[i], dp[rb]);
+    }
+    f32x4 pv[4], dsv[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * rb + 4 * g + j;  // row within the tile
+        float arg = fmaf(s[rb][j], c2, -lbuf[par][rr]);
+        if (BIAS) {
+          const int r = min(q0 + rr, Nq - 1);
+          arg = fmaf(bias[(bh * Nq + r) * (size_t)Nk + min(key, Nk - 1)], kLog2e, arg);
+        }
+        float p = fast_exp2(arg);
+        if (masked && key >= ebuf[par][rr]) p = 0.f;
+        pv[rb][j] = p;
+        dsv[rb][j] = p * (dp[rb][j] - cbuf[par][rr]);
+      }
+    }
+    // dV^T += G^T P and dK^T += Q^T D over the tile's two 32-row steps
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const bf16x8 pop = pack_b(pv[2 * k2], pv[2 * k2 + 1]);
+      const bf16x8 dop = pack_b(dsv[2 * k2], dsv[2 * k2 + 1]);
+#pragma unroll
+      for (int db = 0; db < DV / 16; ++db)
+        acc_v[db] = mfma(tr_read(gt_l + ga.tr[db] + 32 * k2 * Tile<DV>::ROW, 16 * Tile<DV>::ROW), pop, acc_v[db]);
+#pragma unroll
+      for (int db = 0; db < DK / 16; ++db)
+        acc_k[db] = mfma(tr_read(qt_l + qa.tr[db] + 32 * k2 * Tile<DK>::ROW, 16 * Tile<DK>::ROW), dop, acc_k[db]);
+    }
+  }
+
+  if (kvalid) {
+    uint16_t* ov = dv + (bh * Nk + key) * (size_t)DV;
+    uint16_t* ok = dk + (bh * Nk + key) * (size_t)DK;
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d) {
+      u32x2 w;
+      w[0] = cvt_pk_bf16(acc_v[d][0], acc_v[d][1]);
+      w[1] = cvt_pk_bf16(acc_v[d][2], acc_v[d][3]);
+      *reinterpret_cast<u32x2*>(ov + 16 * d + 4 * g) = w;
+    }
+#pragma unroll
+    for (int d = 0; d < DK / 16; ++d) {
+      u32x2 w;
+      w[0] = cvt_pk_bf16(acc_k[d][0] * scale, acc_k[d][1] * scale);
+      w[1] = cvt_pk_bf16(acc_k[d][2] * scale, acc_k[d][3] * scale);
+      *reinterpret_cast<u32x2*>(ok + 16 * d + 4 * g) = w;
+    }
+  }
+}
+
+template <int DK, int DV, bool BIAS>
+hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
+  const unsigned bh = (unsigned)(a.B * a.H);
+  if (a.Nk > 0)
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nk + kTile - 1) / kTile), bh),
+                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dk_out,
+                       (uint16_t*)a.dv_out, a.H, a.Nq, a.Nk, a.scale, a.causal);
+  if ((long long)a.B * a.H * a.Nq > 0)
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
+                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dq_out, a.H, a.Nq,
+                       a.Nk, a.scale, a.causal);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_b(const BwdArgs& a, hipStream_t s) {
+  return a.bias ? launch_t<DK, DV, true>(a, s) : launch_t<DK, DV, false>(a, s);
+}
+
+}  // namespace
+
+bool bwd_bf16_mfma_eligible(const BwdArgs& a) {
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && aligned(a.q) && aligned(a.k) &&
+         aligned(a.v) && aligned(a.dout) && aligned(a.dq_out) && aligned(a.dk_out) && aligned(a.dv_out);
+}
+
+hipError_t launch_bwd_bf16_mfma(const BwdArgs& a, hipStream_t s) {
+  if (a.dk == 64 && a.dv == 64) return launch_b<64, 64>(a, s);
+  if (a.dk == 64) return launch_b<64, 128>(a, s);
+  if (a.dv == 64) return launch_b<128, 64>(a, s);
+  return launch_b<128, 128>(a, s);
+}
+
+}  // namespace fa

@@ -61,7 +61,11 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_bwd_general_f32(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_general_bf16(const BwdArgs& a, hipStream_t stream);
+// backward: c = dO.O, then dK/dV and dQ (bf16 with head dims 64/128 and
+// 16-byte aligned tensors on the matrix cores, everything else general)
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+bool bwd_bf16_mfma_eligible(const BwdArgs& a);
+hipError_t launch_bwd_bf16_mfma(const BwdArgs& a, hipStream_t stream);  // after c is formed
 
 }  // namespace fa
