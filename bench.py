@@ -6,7 +6,8 @@
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in device memory: one fa_fwd call for the prefill and
 long-context workloads, one fa_decode_splitk call (partial + merge kernels)
-for decode.  W untimed steps, then exactly K timed steps between device
+for decode, one fa_bwd call (c, dK/dV, dQ kernels; O and lse from one
+untimed fa_fwd) for the backward workload.  W untimed steps, then exactly K timed steps between device
 synchronisations; the JSON line on stdout reports the main workload
 (default: causal bf16 prefill 4x32x4096^2, d=128) and, under "secondary",
 the long-context and decode workloads measured the same way.
@@ -14,6 +15,9 @@ the long-context and decode workloads measured the same way.
 Algorithmic work (what the method must do, not what a kernel happens to do):
 * prefill / long: FLOPs = 2 (dk + dv) x (number of allowed query-key pairs);
   exponentials and maxima are not counted;
+* backward: FLOPs = 2 (3 dk + 2 dv) x (allowed pairs): the five products
+  S = QK^T, dP = G V^T, dV = P^T G, dK = D^T Q, dQ = D K ([GS] section 7);
+  recomputing S and dP in both the dK/dV and the dQ kernel is not counted;
 * decode: bytes = the K/V rows actually read (sum over sequences of
   H * k_len * (dk + dv) * 2) + q + o (2 bytes each) + lse (4 bytes); the
   split-K workspace is not counted.
@@ -50,9 +54,12 @@ KERNEL_SOURCES = {
     "prefill": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+    "backward": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
+                 "online_softmax_05_amd/csrc/fa_common.h"],
 }
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
-                "decode": "decode_partial_fast_kernel + decode_merge_kernel"}
+                "decode": "decode_partial_fast_kernel + decode_merge_kernel",
+                "backward": "bwd_dot_kernel + bwd_dkdv_bf16_kernel<128, 128, false> + bwd_dq_bf16_kernel<128, 128, false>"}
 
 
 def log(msg):
@@ -238,6 +245,76 @@ def run_prefill(name, args, dev):
     return res
 
 
+def cpu_baseline_backward(inp, budget_s):
+    import numpy as np
+
+    import oracle
+
+    q, k, v, g = inp["q"], inp["k"], inp["v"], inp["g"]
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    scale = float(np.float32(inp["scale"]))
+    flops = 0.0
+    heads = 0
+    elapsed = 0.0  # oracle time only (it rebuilds its own forward); input copies excluded
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        qh, kh, vh, gh = (t[b, h].double().cpu().numpy() for t in (q, k, v, g))
+        ts = time.perf_counter()
+        oracle.attention_bwd_head(qh, kh, vh, gh, scale=scale, nq=N, causal=True)
+        elapsed += time.perf_counter() - ts
+        flops += 2.0 * (3 * dk + 2 * dv) * causal_pairs(N, N)
+        heads += 1
+        if elapsed >= budget_s:
+            break
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"{heads} of {B * H} heads of the backward workload, dense float64 numpy oracle "
+                       f"(forward included), {elapsed:.1f} s of oracle time (input copies excluded)",
+                seconds=elapsed, cpu=platform.processor() or platform.machine())
+
+
+def run_backward(args, dev):
+    import torch
+
+    import online_softmax_05_amd as fa
+    import workloads
+
+    log("backward: drawing inputs on the device")
+    inp = workloads.backward(dev)
+    s = workloads.SHAPES["backward"]
+    B, H, N, dk, dv = s["B"], s["H"], s["Nq"], s["dk"], s["dv"]
+    o, lse = fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True)
+    dq, dk_, dv_ = torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"])
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_bwd(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True, dq=dq, dk=dk_,
+                  dv=dv_, workspace=ws)
+
+    log(f"backward: timing {args.warmup} + {args.steps} steps")
+    t = time_launches(step, args.steps, args.warmup)
+    pairs = B * H * causal_pairs(N, N)
+    flops = 2.0 * (3 * dk + 2 * dv) * pairs
+    value = flops / (t["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (t["launch_ms_mean"] * 1e-3) / 1e12
+    res = dict(
+        workload=workloads.DESCRIPTIONS["backward"], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
+        frac_of_peak=value / PEAK_BF16_TFLOPS,
+        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=stored_traffic("backward"),
+                      kernel=KERNEL_NAMES["backward"], launch_ms_mean=t["launch_ms_mean"],
+                      launch_ms_median=t["launch_ms_median"], algorithmic_flops_per_launch=flops),
+        config=dict(workload=workloads.DESCRIPTIONS["backward"], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
+                    dtype="bf16", allowed_pairs=pairs),
+    )
+    if not args.no_cpu_baseline:
+        log("backward: timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_backward(inp, args.cpu_budget)
+    del inp, o, lse, dq, dk_, dv_, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(args, dev):
     import torch
 
@@ -300,7 +377,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["prefill", "long", "decode"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "decode", "backward"], default="prefill")
     ap.add_argument("--only", action="store_true", help="measure only the main workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -325,10 +402,12 @@ def main():
         copy_calibration(dev)
         return
 
-    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode") if w != args.workload])
+    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "backward")
+                                                      if w != args.workload])
+    runners = {"decode": run_decode, "backward": run_backward}
     results = {}
     for w in order:
-        results[w] = run_decode(args, dev) if w == "decode" else run_prefill(w, args, dev)
+        results[w] = runners[w](args, dev) if w in runners else run_prefill(w, args, dev)
 
     main_res = results[args.workload]
     line = {

@@ -274,8 +274,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s) { return launch_gener
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   if (!bwd_bf16_mfma_eligible(a)) return launch_general<uint16_t>(a, s);
-  launch_dot<uint16_t>(a, s);
-  return launch_bwd_bf16_mfma(a, s);
+  return launch_bwd_bf16_mfma(a, s);  // forms c itself
 }
 
 }  // namespace fa

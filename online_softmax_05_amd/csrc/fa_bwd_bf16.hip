@@ -10,8 +10,10 @@
 //   D_ij = p_ij (g_i . v_j - c_i)
 //   dV = P^T G,   dK = scale D^T Q,   dQ = scale D K
 //
-// Two kernels after the per-row c (bwd_dot_kernel, general file); neither
-// uses atomics, so the results are bitwise reproducible.
+// Two kernels, dQ first: it also forms c_i for its rows (each lane holds a
+// quarter of a row of G and of O) and stores it for the dK/dV kernel that
+// follows on the same stream.  Neither uses atomics, so the results are
+// bitwise reproducible.
 //
 // dQ kernel: one work-group = 4 waves = 64 query rows of one (batch, head),
 // 16 rows per wave with their Q and G rows held as MFMA operands.  Key tiles
@@ -157,7 +159,8 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
 template <int DK, int DV, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ cvec,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ cvec,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dq, int H, int Nq,
     int Nk, float scale, int causal) {
   // one array, buffers addressed by offset (a runtime-indexed table of
@@ -190,7 +193,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const float l_row = rvalid ? lse[bh * Nq + row] : kNegInf;
   const bool live = l_row != kNegInf;  // rows without an allowed key contribute nothing
   const float l2 = live ? l_row * kLog2e : 0.f;
-  const float c_row = rvalid ? cvec[bh * Nq + row] : 0.f;
+  // c_i = g_i . o_i: this lane's quarter of the row (dims 32t + 8g .. +7),
+  // then the four lanes r16, r16 + 16, r16 + 32, r16 + 48 of the row
+  float c_row = 0.f;
+  {
+    bf16x8 of[DV / 32];
+    load_rows_b<DV>(of, o + bh * Nq * DV, row, rvalid, g);
+#pragma unroll
+    for (int t = 0; t < DV / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c_row = fmaf((float)gf[t][e], (float)of[t][e], c_row);
+    c_row += __shfl_xor(c_row, 16);
+    c_row += __shfl_xor(c_row, 32);
+    if (rvalid && g == 0) cvec[bh * Nq + row] = c_row;
+  }
   const float c2 = scale * kLog2e;
   const int row_end = !live ? 0 : (causal ? min(klen, row + shift + 1) : klen);
   const float* brow = BIAS ? bias + (bh * Nq + (size_t)(rvalid ? row : 0)) * Nk : nullptr;
@@ -423,16 +439,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
 template <int DK, int DV, bool BIAS>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
+  // dQ first: it stores c for the dK/dV kernel
+  if ((long long)a.B * a.H * a.Nq > 0)
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
+                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len,
+                       (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, a.causal);
   if (a.Nk > 0)
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nk + kTile - 1) / kTile), bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dk_out,
                        (uint16_t*)a.dv_out, a.H, a.Nq, a.Nk, a.scale, a.causal);
-  if ((long long)a.B * a.H * a.Nq > 0)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
-                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dq_out, a.H, a.Nq,
-                       a.Nk, a.scale, a.causal);
   return hipGetLastError();
 }
 

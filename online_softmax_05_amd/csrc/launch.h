@@ -66,6 +66,6 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 bool bwd_bf16_mfma_eligible(const BwdArgs& a);
-hipError_t launch_bwd_bf16_mfma(const BwdArgs& a, hipStream_t stream);  // after c is formed
+hipError_t launch_bwd_bf16_mfma(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

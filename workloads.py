@@ -40,6 +40,7 @@ SHAPES = {
     "prefill": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
     "long": dict(B=1, H=16, Nq=16384, Nk=16384, dk=128, dv=128),
     "decode": dict(B=64, H=32, Nq=1, Nk=8192, dk=128, dv=128),
+    "backward": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
 }
 
 DESCRIPTIONS = {
@@ -48,6 +49,7 @@ DESCRIPTIONS = {
     "prefill": "attention fwd prefill 4x32x4096x4096 d128 bf16 causal",
     "long": "attention fwd long context 1x16x16384x16384 d128 bf16 causal, Q,K ~ N(0,16)",
     "decode": "split-K decode 64x32 queries, KV lengths U[1,8192], d128 bf16, 512-key chunks",
+    "backward": "attention bwd (dQ, dK, dV by recomputation) 4x32x4096x4096 d128 bf16 causal, upstream gradient N(0,1)",
 }
 
 
@@ -105,6 +107,17 @@ def prefill(device):
     k = _randn_dev(g, (s["B"], s["H"], s["Nk"], s["dk"]), device, torch.bfloat16)
     v = _randn_dev(g, (s["B"], s["H"], s["Nk"], s["dv"]), device, torch.bfloat16)
     return dict(q=q, k=k, v=v, bias=None, k_len=None, causal=True, scale=1.0 / math.sqrt(128), block_n=0)
+
+
+def backward(device):
+    """The prefill workload's Q, K, V (same seed, same draws) plus an upstream
+    gradient dLoss/dO ~ N(0, 1) from a second generator (seed 200 + the
+    prefill seed)."""
+    inp = prefill(device)
+    s = SHAPES["backward"]
+    g = torch.Generator(device=device).manual_seed(200 + SEEDS["prefill"])
+    inp["g"] = _randn_dev(g, (s["B"], s["H"], s["Nq"], s["dv"]), device, torch.bfloat16)
+    return inp
 
 
 def long(device):
