@@ -6,8 +6,9 @@
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in device memory: one fa_fwd call for the prefill and
 long-context workloads, one fa_decode_splitk call (partial + merge kernels)
-for decode, one fa_bwd call (c, dK/dV, dQ kernels; O and lse from one
-untimed fa_fwd) for the backward workload.  W untimed steps, then exactly K timed steps between device
+for decode, one fa_decode_splitk_mq call for the multi-query decode, one
+fa_bwd call (dQ then dK/dV kernels; O and lse from one untimed fa_fwd) for
+the backward workload.  W untimed steps, then exactly K timed steps between device
 synchronisations; the JSON line on stdout reports the main workload
 (default: causal bf16 prefill 4x32x4096^2, d=128) and, under "secondary",
 the long-context and decode workloads measured the same way.
@@ -20,7 +21,8 @@ Algorithmic work (what the method must do, not what a kernel happens to do):
   recomputing S and dP in both the dK/dV and the dQ kernel is not counted;
 * decode: bytes = the K/V rows actually read (sum over sequences of
   H * k_len * (dk + dv) * 2) + q + o (2 bytes each) + lse (4 bytes); the
-  split-K workspace is not counted.
+  split-K workspace is not counted; the multi-query decode counts the same
+  K/V bytes plus Nq rows of q, o and lse;
 
 roofline.achieved divides that work per launch by the kernel's mean duration
 measured with HIP events recorded on the launch stream around every timed
@@ -55,11 +57,14 @@ KERNEL_SOURCES = {
     "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "backward": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
-                 "online_softmax_05_amd/csrc/fa_common.h"],
+                 "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h"],
+    "decode_mq": ["online_softmax_05_amd/csrc/fa_decode_mq.hip", "online_softmax_05_amd/csrc/fa_tiles.h",
+                  "online_softmax_05_amd/csrc/fa_common.h"],
 }
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
-                "backward": "bwd_dot_kernel + bwd_dkdv_bf16_kernel<128, 128, false> + bwd_dq_bf16_kernel<128, 128, false>"}
+                "backward": "bwd_dq_bf16_kernel<128, 128, false> + bwd_dkdv_bf16_kernel<128, 128, false>",
+                "decode_mq": "mq_partial_bf16_kernel + mq_merge_kernel"}
 
 
 def log(msg):
@@ -315,6 +320,47 @@ def run_backward(args, dev):
     return res
 
 
+def run_decode_mq(args, dev):
+    import torch
+
+    import online_softmax_05_amd as fa
+    import workloads
+
+    log("decode_mq: drawing inputs on the device")
+    inp = workloads.decode_mq(dev)
+    s = workloads.SHAPES["decode_mq"]
+    B, H, Nq, Nk, dk, dv = s["B"], s["H"], s["Nq"], s["Nk"], s["dk"], s["dv"]
+    chunk = inp["chunk"]
+    ws = torch.empty(fa.fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk, dv, chunk) // 4, dtype=torch.float32,
+                     device=dev)
+    out = torch.empty((B, H, Nq, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_decode_splitk_mq(inp["q"], inp["k"], inp["v"], inp["k_len"], causal=True, scale=inp["scale"],
+                               chunk=chunk, out=out, lse=lse, workspace=ws)
+
+    log(f"decode_mq: timing {args.warmup} + {args.steps} steps")
+    t = time_launches(step, args.steps, args.warmup)
+    kl = inp["k_len_host"].long()
+    nbytes = float(H * kl.sum().item() * (dk + dv) * 2 + B * H * Nq * (dk * 2 + dv * 2 + 4))
+    value = nbytes / (t["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (t["launch_ms_mean"] * 1e-3) / 1e9
+    res = dict(
+        workload=workloads.DESCRIPTIONS["decode_mq"], value=value, unit="GB/s", ms_per_step=t["ms_per_step"],
+        frac_of_peak=value / PEAK_HBM_GBS,
+        roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
+                      traffic=stored_traffic("decode_mq"), kernel=KERNEL_NAMES["decode_mq"],
+                      launch_ms_mean=t["launch_ms_mean"], launch_ms_median=t["launch_ms_median"],
+                      algorithmic_bytes_per_launch=nbytes),
+        config=dict(workload=workloads.DESCRIPTIONS["decode_mq"], B=B, H=H, Nq=Nq, Nk_max=Nk, dk=dk, dv=dv,
+                    chunk=chunk, causal=True, dtype="bf16", k_len_sum=int(kl.sum().item())),
+    )
+    del inp, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(args, dev):
     import torch
 
@@ -377,7 +423,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["prefill", "long", "decode", "backward"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "decode", "decode_mq", "backward"], default="prefill")
     ap.add_argument("--only", action="store_true", help="measure only the main workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -402,9 +448,9 @@ def main():
         copy_calibration(dev)
         return
 
-    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "backward")
+    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "decode_mq", "backward")
                                                       if w != args.workload])
-    runners = {"decode": run_decode, "backward": run_backward}
+    runners = {"decode": run_decode, "decode_mq": run_decode_mq, "backward": run_backward}
     results = {}
     for w in order:
         results[w] = runners[w](args, dev) if w in runners else run_prefill(w, args, dev)

@@ -128,6 +128,53 @@ int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
                      float scale, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * Bytes of fp32 workspace fa_decode_splitk_mq needs:
+ *   B * H * ceil(Nk_max / chunk) * Nq * (dv + 2) * 4.
+ * Returns 0 for invalid arguments (negative sizes, Nq outside 1..16, chunk
+ * not a positive multiple of 64).
+ */
+size_t fa_decode_splitk_mq_workspace_bytes(int B, int H, int Nq, int Nk_max,
+                                           int dv, int chunk);
+
+/*
+ * fa_decode_splitk_mq -- split-KV attention for a few query rows per
+ * sequence against a KV cache (chunked prefill, several speculative tokens):
+ * the key axis split into chunks ([GS] section 8, split KV loading for short
+ * queries), chunk states merged per row with the rule of [GS] section 4 /
+ * [VW] Step 5.
+ *
+ *   q       [B, H, Nq, dk]     dtype, 1 <= Nq <= 16: the LAST Nq positions
+ *                              of each sequence
+ *   k_cache [B, H, Nk_max, dk] dtype   only keys j < k_len[b] are read
+ *   v_cache [B, H, Nk_max, dv] dtype
+ *   k_len   [B] int32, required; clamped to [0, Nk_max]
+ *   o       [B, H, Nq, dv] dtype; lse [B, H, Nq] fp32 or NULL
+ *   causal  0: every row sees the k_len[b] keys; 1: row i sees keys
+ *           j <= i + k_len[b] - Nq (bottom-right alignment against the
+ *           sequence's own length, [GS] section 6); rows left with no key
+ *           get o = 0, lse = -inf
+ *   chunk   a positive multiple of 64, at most 2048 (512 usual)
+ *   workspace: at least fa_decode_splitk_mq_workspace_bytes(...) bytes,
+ *              16-byte aligned; contents on entry are ignored.
+ * Two kernels on `stream`: the chunk states (one work-group per chunk, batch
+ * and head, chunks below k_len[b] only), then one merge per (b, h, row) in
+ * ascending chunk order.
+ */
+int fa_decode_splitk_mq(const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* k_len, void* o,
+                        float* lse, int B, int H, int Nq, int Nk_max, int dk,
+                        int dv, int chunk, int dtype, float scale, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only validation of fa_decode_splitk_mq's arguments. */
+int fa_check_decode_mq(const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* k_len,
+                       const void* o, const float* lse, int B, int H, int Nq,
+                       int Nk_max, int dk, int dv, int chunk, int dtype,
+                       float scale, int causal, const void* workspace,
+                       size_t workspace_bytes);
+
 /* Host-only validation of fa_decode_splitk's arguments. */
 int fa_check_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* k_len, const void* o, const float* lse,

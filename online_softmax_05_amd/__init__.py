@@ -25,6 +25,7 @@ __all__ = [
     "FA_F32", "FA_BF16", "FaError", "lib", "lib_path",
     "fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
     "fa_check_fwd", "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
+    "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes", "fa_check_decode_mq",
     "fa_status_str", "fa_abi_version",
 ]
 
@@ -45,6 +46,10 @@ _SIGNATURES = {
     "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
+    "fa_decode_splitk_mq_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_splitk_mq": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                                 _vp]),
+    "fa_check_decode_mq": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _ip, _vp, _vp, _vp,
                     _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
@@ -286,3 +291,49 @@ def fa_bwd(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=F
     if st != 0:
         raise FaError(st)
     return dq, dk, dv
+
+
+def fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk_max, dv, chunk=512):
+    return lib().fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk_max, dv, chunk)
+
+
+def fa_check_decode_mq(q, k, v, k_len, o, lse, B, H, Nq, Nk_max, dk, dv, chunk, dtype, scale, causal, workspace,
+                       workspace_bytes):
+    """Host-only validation (integer addresses; nothing is dereferenced)."""
+    return lib().fa_check_decode_mq(q, k, v, k_len, o, lse, B, H, Nq, Nk_max, dk, dv, chunk, dtype, float(scale),
+                                    causal, workspace, workspace_bytes)
+
+
+def fa_decode_splitk_mq(q, k_cache, v_cache, k_len, *, causal=True, scale=None, chunk=512, out=None, lse=None,
+                        workspace=None, want_lse=True):
+    """Split-KV attention of Nq <= 16 query rows per sequence (the sequence's
+    last Nq positions): q [B,H,Nq,dk], caches [B,H,Nk_max,d], k_len int32 [B].
+    Returns (o [B,H,Nq,dv], lse [B,H,Nq])."""
+    _need(q, "q", dims=4)
+    dev = q.device
+    _need(k_cache, "k_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(v_cache, "v_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(k_len, "k_len", dtype=torch.int32, dims=1, device=dev)
+    B, H, Nq, dk = q.shape
+    Nk, dv = k_cache.shape[2], v_cache.shape[3]
+    if tuple(k_cache.shape) != (B, H, Nk, dk) or tuple(v_cache.shape) != (B, H, Nk, dv):
+        raise FaError(2, "cache shapes do not match q")
+    if k_len.shape[0] != B:
+        raise FaError(2, f"k_len must have {B} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    need = fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    else:
+        _need(workspace, "workspace", dtype=torch.float32, dims=1, device=dev)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    st = lib().fa_decode_splitk_mq(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_len), _ptr(out), _ptr(lse),
+                                   B, H, Nq, Nk, dk, dv, int(chunk), _dtype_code(q), float(scale),
+                                   int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(dev))
+    if st != 0:
+        raise FaError(st)
+    return out, lse

@@ -77,6 +77,31 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* k_l
   return FA_OK;
 }
 
+int check_decode_mq(const void* q, const void* k, const void* v, const int32_t* k_len, const void* o,
+                    const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int chunk, int dtype, float scale,
+                    int causal, const void* workspace, size_t workspace_bytes) {
+  (void)lse;
+  if (B < 0 || H < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (Nq < 1 || Nq > 16) return FA_ERR_UNSUPPORTED;
+  if (dk < 1 || dv < 1) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dk > kMaxHeadDim || dv > kMaxHeadDim) return FA_ERR_UNSUPPORTED;
+  if (chunk < 64 || chunk > kMaxChunk || chunk % 64 != 0) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
+  const long long max_chunks = (Nk + (long long)chunk - 1) / chunk;
+  if (!product_fits({B, H, std::max(max_chunks, 1LL), Nq}, kInt32Max)) return FA_ERR_SHAPE;
+  if ((long long)B * H == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || k_len == nullptr) return FA_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
+  const size_t need = fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk, dv, chunk);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return FA_ERR_WORKSPACE;
+  }
+  return FA_OK;
+}
+
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
               const float* bias, const int32_t* k_len, const void* dq, const void* dk, const void* dv, int B, int H,
               int Nq, int Nk, int d_k, int d_v, int dtype, float scale, int causal, const void* workspace,
@@ -109,7 +134,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 extern "C" {
 
-int fa_abi_version(void) { return 101; }
+int fa_abi_version(void) { return 102; }
 
 const char* fa_status_str(int status) {
   switch (status) {
@@ -171,6 +196,36 @@ int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache, co
                    ws, ws == nullptr ? nullptr : ws + (size_t)B * H * max_chunks * dv, max_chunks};
   const hipError_t e = dtype == FA_BF16 ? fa::launch_decode_bf16(a, static_cast<hipStream_t>(stream))
                                         : fa::launch_decode_f32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_splitk_mq_workspace_bytes(int B, int H, int Nq, int Nk_max, int dv, int chunk) {
+  if (B < 0 || H < 0 || Nq < 1 || Nq > 16 || Nk_max < 0 || dv < 1 || chunk < 64 || chunk % 64 != 0) return 0;
+  const size_t max_chunks = ((size_t)Nk_max + chunk - 1) / chunk;
+  return (size_t)B * H * max_chunks * Nq * ((size_t)dv + 2) * sizeof(float);
+}
+
+int fa_check_decode_mq(const void* q, const void* k_cache, const void* v_cache, const int32_t* k_len, const void* o,
+                       const float* lse, int B, int H, int Nq, int Nk_max, int dk, int dv, int chunk, int dtype,
+                       float scale, int causal, const void* workspace, size_t workspace_bytes) {
+  return check_decode_mq(q, k_cache, v_cache, k_len, o, lse, B, H, Nq, Nk_max, dk, dv, chunk, dtype, scale, causal,
+                         workspace, workspace_bytes);
+}
+
+int fa_decode_splitk_mq(const void* q, const void* k_cache, const void* v_cache, const int32_t* k_len, void* o,
+                        float* lse, int B, int H, int Nq, int Nk_max, int dk, int dv, int chunk, int dtype, float scale,
+                        int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_decode_mq(q, k_cache, v_cache, k_len, o, lse, B, H, Nq, Nk_max, dk, dv, chunk, dtype, scale,
+                                 causal, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0) return FA_OK;
+  const int max_chunks = (int)(((long long)Nk_max + chunk - 1) / chunk);
+  float* ws = static_cast<float*>(workspace);
+  fa::DecodeMqArgs a{q,     k_cache, v_cache, k_len, o,      lse,   B,  H,
+                     Nq,    Nk_max,  dk,      dv,    chunk,  scale, causal,
+                     ws,    ws == nullptr ? nullptr : ws + (size_t)B * H * max_chunks * Nq * dv, max_chunks};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_decode_mq_bf16(a, s) : fa::launch_decode_mq_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -32,100 +32,24 @@
 // P and D are rounded to bf16 only as matrix-core operands; every sum is
 // fp32.
 #include "fa_common.h"
+#include "fa_tiles.h"
 #include "launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 64;  // rows of every LDS tile (keys or queries)
+constexpr int kThreads = 64 * tiles::kWaves;
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) float lds_float;
-typedef const __attribute__((address_space(1))) void gbl_void;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS tile of kTile rows x D bf16, row-major, 16-byte chunk c of row r stored
-// at chunk position c ^ swz(r % 16): the 16 rows of an operand read land on
-// 16 distinct 16-byte bank positions (128-bit reads are served 16 lanes at a
-// time over 256 bytes of banks) and the 8 rows of a transposed read on 8
-// distinct 32-byte chunk pairs.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
-}
-
-template <int D>
-struct Tile {
-  static constexpr int R = D / 8;   // 16-byte chunks per row
-  static constexpr int ROW = R * 16;
-  static constexpr int BYTES = kTile * ROW;
-  static constexpr int IPW = kTile * R / 64 / kWaves;  // 1 KiB direct loads per wave
-};
-
-// Per-lane address parts for one tile layout D.
-template <int D>
-struct TileAddr {
-  int frag[D / 32];  // operand read (tile row 16blk + r16, dims 32t + 8g .. +7): + 16 blk ROW
-  int tr[D / 16];    // transposed read of dim block db (tile rows 32kt + 16h + 4g + e): + (32kt + 16h) ROW
-  int ld[Tile<D>::IPW];
-
-  __device__ __forceinline__ void init(int lane, int wave) {
-    constexpr int ROW = Tile<D>::ROW;
-    const int r16 = lane & 15, g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) frag[t] = r16 * ROW + 16 * ((4 * t + g) ^ swz<D>(r16));
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      tr[db] = (4 * g + e) * ROW + 16 * ((2 * db + (r >> 1)) ^ swz<D>(4 * g + e)) + 8 * (r & 1);
-#pragma unroll
-    for (int i = 0; i < Tile<D>::IPW; ++i) {
-      const int slot = (wave * Tile<D>::IPW + i) * 64 + lane;
-      const int row = slot / Tile<D>::R;
-      ld[i] = row * D + ((slot % Tile<D>::R) ^ swz<D>(row)) * 8;
-    }
-  }
-};
-
-// Direct-to-LDS load of this wave's share of a tile whose first row is `src`
-// (rows_left rows remain in the tensor); rows past the end re-read the last
-// row, so no lane reads out of bounds (those rows are masked).
-template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int rows_left, const TileAddr<D>& a, lds_char* dst,
-                                          int wave) {
-  constexpr int IPW = Tile<D>::IPW;
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    int off = a.ld[i];
-    if (rows_left < kTile) {
-      const int row = off / D;
-      off += (min(row, rows_left - 1) - row) * D;
-    }
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ bf16x8 frag_read(const lds_char* p) { return *(const lds_bf16x8*)p; }
-
-__device__ __forceinline__ bf16x8 tr_read(const lds_char* p, int row_bytes16) {
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + row_bytes16));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
+using tiles::kTile;
+using tiles::kWaves;
+using tiles::Tile;
+using tiles::TileAddr;
+using tiles::lds_char;
+using tiles::cvt_pk_bf16;
+using tiles::frag_read;
+using tiles::load_tile;
+using tiles::tr_read;
+using tiles::wait_loads;
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -53,6 +53,21 @@ struct BwdArgs {
   int causal;
 };
 
+struct DecodeMqArgs {
+  const void* q;  // [B, H, Nq, dk]
+  const void* k;
+  const void* v;
+  const int32_t* k_len;
+  void* o;     // [B, H, Nq, dv]
+  float* lse;  // [B, H, Nq] or null
+  int B, H, Nq, Nk, dk, dv, chunk;
+  float scale;
+  int causal;
+  float* ws_u;   // [B*H*max_chunks*Nq, dv]
+  float* ws_ml;  // [B*H*max_chunks*Nq, 2]
+  int max_chunks;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // fast bf16 path: head dims 64/128, 16-byte aligned tensors, 64-key tiles
@@ -61,6 +76,8 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mq_bf16(const DecodeMqArgs& a, hipStream_t stream);
+hipError_t launch_decode_mq_f32(const DecodeMqArgs& a, hipStream_t stream);
 // backward: c = dO.O, then dK/dV and dQ (bf16 with head dims 64/128 and
 // 16-byte aligned tensors on the matrix cores, everything else general)
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);

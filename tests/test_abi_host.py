@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol():
     names = header_functions()
     assert {"fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes", "fa_check_fwd",
             "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd", "fa_status_str",
-            "fa_abi_version"} <= set(names)
+            "fa_abi_version", "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes",
+            "fa_check_decode_mq"} <= set(names)
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
@@ -59,7 +60,7 @@ def test_header_is_plain_c():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 101
+    assert fa.fa_abi_version() == 102
     for st in range(6):
         assert isinstance(fa.fa_status_str(st), str) and fa.fa_status_str(st)
     assert fa.fa_status_str(0) == "ok"
@@ -186,6 +187,39 @@ def test_bwd_workspace_bytes():
 ])
 def test_check_bwd(kw, want):
     assert check_bwd(**kw) == want
+
+
+def check_mq(**kw):
+    a = dict(q=P, k=P, v=P, k_len=P, o=P, lse=P, B=4, H=2, Nq=4, Nk=1000, dk=128, dv=64, chunk=512,
+             dtype=fa.FA_BF16, scale=0.1, causal=1, ws=P, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = fa.fa_decode_splitk_mq_workspace_bytes(a["B"], a["H"], a["Nq"], a["Nk"], a["dv"], a["chunk"])
+    return fa.fa_check_decode_mq(a["q"], a["k"], a["v"], a["k_len"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                 a["Nk"], a["dk"], a["dv"], a["chunk"], a["dtype"], a["scale"], a["causal"],
+                                 a["ws"], a["ws_bytes"])
+
+
+def test_mq_workspace_bytes():
+    f = fa.fa_decode_splitk_mq_workspace_bytes
+    assert f(2, 3, 4, 1000, 64, 512) == 2 * 3 * 2 * 4 * 66 * 4
+    assert f(1, 1, 17, 100, 8, 64) == 0 and f(1, 1, 0, 100, 8, 64) == 0   # Nq outside 1..16
+    assert f(1, 1, 2, 100, 8, 100) == 0                                   # chunk not a multiple of 64
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, OK), ({"dtype": fa.FA_F32}, OK), ({"lse": None}, OK), ({"causal": 0}, OK), ({"Nq": 1}, OK),
+    ({"Nq": 16}, OK), ({"Nq": 17}, UNSUP), ({"Nq": 0}, UNSUP), ({"causal": 3}, UNSUP),
+    ({"k_len": None}, NULL), ({"q": None}, NULL), ({"o": None}, NULL), ({"k": None}, NULL),
+    ({"ws": None}, WS), ({"ws_bytes": 100}, WS), ({"ws": P + 8}, WS),
+    ({"chunk": 100}, UNSUP), ({"chunk": 4096}, UNSUP), ({"chunk": 64}, OK),
+    ({"dk": 129}, UNSUP), ({"dv": 0}, SHAPE), ({"B": -1}, SHAPE), ({"Nk": -1}, SHAPE),
+    ({"Nk": 0, "k": None, "v": None, "ws": None, "ws_bytes": 0}, OK),
+    ({"B": 0, "q": None, "o": None, "k_len": None}, OK),
+    ({"scale": math.nan}, UNSUP), ({"dtype": 2}, UNSUP),
+])
+def test_check_decode_mq(kw, want):
+    assert check_mq(**kw) == want
 
 
 def test_binding_fails_loudly_without_a_device():

@@ -20,6 +20,10 @@ Workloads (sizes as [B, H, N, d]):
                   (logit std about 16, the running max rises often), V ~ N(0,1).
 * ``decode``      64x32, one query token, Nk_max=8192, k_len ~ U{1..8192} per
                   sequence, d=128, bf16 N(0,1), split into 512-key chunks.
+* ``decode_mq``   the decode caches and lengths with 4 query rows per
+                  sequence (its last 4 positions, causal), q from seed 305.
+* ``backward``    the prefill Q, K, V plus an upstream gradient dLoss/dO
+                  ~ N(0,1) from seed 203.
 
 Workload k draws Q/K/V from seed k; bias, k_len and the special rows come
 from a second generator seeded 100 + k.  Small workloads are drawn on the CPU
@@ -41,6 +45,7 @@ SHAPES = {
     "long": dict(B=1, H=16, Nq=16384, Nk=16384, dk=128, dv=128),
     "decode": dict(B=64, H=32, Nq=1, Nk=8192, dk=128, dv=128),
     "backward": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
+    "decode_mq": dict(B=64, H=32, Nq=4, Nk=8192, dk=128, dv=128),
 }
 
 DESCRIPTIONS = {
@@ -50,6 +55,8 @@ DESCRIPTIONS = {
     "long": "attention fwd long context 1x16x16384x16384 d128 bf16 causal, Q,K ~ N(0,16)",
     "decode": "split-K decode 64x32 queries, KV lengths U[1,8192], d128 bf16, 512-key chunks",
     "backward": "attention bwd (dQ, dK, dV by recomputation) 4x32x4096x4096 d128 bf16 causal, upstream gradient N(0,1)",
+    "decode_mq": "split-K multi-query decode 64x32 sequences x 4 query rows (causal), KV lengths U[1,8192], d128 bf16, "
+                 "512-key chunks",
 }
 
 
@@ -140,6 +147,17 @@ def decode(device):
     k_len = torch.randint(1, Nk + 1, (B,), generator=g2, dtype=torch.int64).to(torch.int32)
     return dict(q=q, k=k, v=v, k_len=k_len.to(device), k_len_host=k_len, scale=1.0 / math.sqrt(dk),
                 chunk=512)
+
+
+def decode_mq(device):
+    """The decode workload's caches and lengths (same seeds, same draws) with
+    4 query rows per sequence from a second device generator (seed
+    300 + the decode seed)."""
+    inp = decode(device)
+    s = SHAPES["decode_mq"]
+    g = torch.Generator(device=device).manual_seed(300 + SEEDS["decode"])
+    inp["q"] = _randn_dev(g, (s["B"], s["H"], s["Nq"], s["dk"]), device, torch.bfloat16)
+    return inp
 
 
 def to_device(inputs, device):
