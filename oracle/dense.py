@@ -28,6 +28,14 @@ The allowed set ([GS] sections 1 and 6) is the intersection of
 The causal offset uses the tensor extents Nq and Nk, not k_len: padding is a
 separate key mask ([GS] section 6 treats it as its own mask).
 
+Mask variants ([GS] section 6: top-left alignment as the alternative
+convention; sliding windows need the same alignment audit).  Query row i sits
+at key position pos_i = i + Nk - Nq (bottom-right, the default) or pos_i = i
+(top-left); causal keeps j <= pos_i; a window (wl, wr) keeps
+pos_i - wl <= j (wl given) and j <= pos_i + wr (wr given).  Reading: the
+window is measured from the aligned position, exactly like the causal
+limit, and combines with the other masks by intersection.
+
 Inputs are converted to float64 exactly (bf16 and fp32 values are exactly
 representable); ``scale`` is used as given -- callers pass the float32 value
 the GPU receives.
@@ -38,23 +46,33 @@ import numpy as np
 _ROW_BLOCK = 2048  # rows of S materialised at once; every row is complete
 
 
-def allowed_mask(row_ids, nq, nk, causal, k_len_b):
+def allowed_mask(row_ids, nq, nk, causal, k_len_b, align="bottom_right", window=(None, None)):
     """Boolean [len(row_ids), nk]: True where key j is visible to query row i.
 
-    [GS] section 6: global zero-based positions, bottom-right alignment, and a
-    key-length mask that may empty whole rows or whole tiles.
+    [GS] section 6: global zero-based positions, bottom-right alignment (or
+    top-left), a key-length mask that may empty whole rows or whole tiles,
+    and an optional window (wl, wr) around the aligned position.
     """
     row_ids = np.asarray(row_ids, dtype=np.int64).reshape(-1)
     j = np.arange(nk, dtype=np.int64)[None, :]
     limit = nk if k_len_b is None else min(max(int(k_len_b), 0), nk)
     ok = np.broadcast_to(j < limit, (row_ids.size, nk)).copy()
+    if align not in ("bottom_right", "top_left"):
+        raise ValueError(f"unknown alignment {align!r}")
+    pos = row_ids[:, None] + ((nk - nq) if align == "bottom_right" else 0)
     if causal:
-        ok &= j <= (row_ids[:, None] + (nk - nq))
+        ok &= j <= pos
+    wl, wr = window
+    if wl is not None:
+        ok &= j >= pos - int(wl)
+    if wr is not None:
+        ok &= j <= pos + int(wr)
     return ok
 
 
 def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
-                   bias=None, row_ids=None, return_p=False):
+                   bias=None, row_ids=None, return_p=False, align="bottom_right",
+                   window=(None, None)):
     """Dense attention for selected query rows of one (batch, head).
 
     q: [R, dk] the query rows whose global indices are ``row_ids`` (default
@@ -71,7 +89,7 @@ def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
         row_ids = np.arange(rows)
     row_ids = np.asarray(row_ids, dtype=np.int64)
 
-    ok = allowed_mask(row_ids, nq, nk, causal, k_len_b)
+    ok = allowed_mask(row_ids, nq, nk, causal, k_len_b, align=align, window=window)
     s = (q @ k.T) * float(scale)
     if bias is not None:
         s = s + np.asarray(bias, dtype=np.float64)
@@ -93,7 +111,7 @@ def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
 
 
 def attention_ref(q, k, v, *, scale, causal=False, k_len=None, bias=None,
-                  return_p=False):
+                  return_p=False, align="bottom_right", window=(None, None)):
     """Dense attention over a whole batch: q [B,H,Nq,dk], k [B,H,Nk,dk],
     v [B,H,Nk,dv], k_len [B] or None, bias [B,H,Nq,Nk] or None.
 
@@ -119,7 +137,7 @@ def attention_ref(q, k, v, *, scale, causal=False, k_len=None, bias=None,
                                      scale=scale, nq=nq, causal=causal,
                                      k_len_b=klb, bias=bb,
                                      row_ids=np.arange(r0, r1),
-                                     return_p=return_p)
+                                     return_p=return_p, align=align, window=window)
                 o[b, h, r0:r1] = res[0]
                 lse[b, h, r0:r1] = res[1]
                 if return_p:

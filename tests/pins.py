@@ -233,6 +233,8 @@ def pin_gs_sec6_alignment(orc):
             assert ok[i, :cnt].all() and not ok[i, cnt:].any()
         if "top_left_counts" in case:
             assert case["top_left_counts"] != case["allowed_counts"]
+            tl = orc.allowed_mask(np.arange(nq), nq, nk, True, None, align="top_left")
+            assert list(tl.sum(axis=1)) == case["top_left_counts"], (case, tl)
         # the dense output of an empty row is exactly zero, its lse -inf
         rng = np.random.default_rng(nq * 10 + nk)
         q = rng.standard_normal((nq, 3))
@@ -252,6 +254,49 @@ def pin_gs_sec6_alignment(orc):
     # both masks together intersect; the causal offset uses Nq and Nk
     ok = orc.allowed_mask(np.arange(4), 4, 6, True, 4)
     assert list(ok.sum(axis=1)) == [3, 4, 4, 4]
+
+
+def pin_mask_variants(orc):
+    """Top-left alignment and windows ([GS] section 6), against bands built
+    independently with torch's tril/triu (a key j is visible from row i when
+    pos_i - wl <= j <= pos_i (+ wr)), closed forms, and torch SDPA under that
+    band."""
+    import torch
+
+    rng = np.random.default_rng(61)
+    for (nq, nk, align, wl, wr, causal, k_len) in (
+            (7, 11, "bottom_right", 3, None, True, None), (7, 11, "top_left", 3, None, True, None),
+            (9, 6, "bottom_right", 2, None, True, 5), (6, 9, "top_left", None, None, True, 8),
+            (8, 8, "bottom_right", 2, 1, False, None), (5, 12, "top_left", 0, 4, False, 10),
+            (10, 10, "bottom_right", 0, None, True, None)):
+        off = (nk - nq) if align == "bottom_right" else 0
+        band = torch.ones(nq, nk, dtype=torch.bool)
+        if causal:
+            band = band.tril(diagonal=off)
+        if wr is not None:
+            band = band.tril(diagonal=off + wr)
+        if wl is not None:
+            band = band.triu(diagonal=off - wl)
+        if k_len is not None:
+            band[:, min(max(k_len, 0), nk):] = False
+        ok = orc.allowed_mask(np.arange(nq), nq, nk, causal, k_len, align=align, window=(wl, wr))
+        assert np.array_equal(ok, band.numpy()), (nq, nk, align, wl, wr, causal, k_len)
+        q = rng.standard_normal((1, 1, nq, 4))
+        k = rng.standard_normal((1, 1, nk, 4))
+        v = rng.standard_normal((1, 1, nk, 3))
+        o, lse = orc.attention_ref(q, k, v, scale=0.7, causal=causal, k_len=None if k_len is None else [k_len],
+                                   align=align, window=(wl, wr))
+        rows = band.any(dim=1).numpy()
+        add = np.where(band.numpy(), 0.0, -np.inf)[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(add),
+            scale=0.7).numpy()
+        _close(o[0, 0, rows], ref[0, 0, rows], 1e-12, "window vs SDPA")
+        assert np.all(o[0, 0, ~rows] == 0.0) and np.all(lse[0, 0, ~rows] == -np.inf)
+        if causal and wl == 0:  # a row sees exactly the key at its aligned position
+            for i in range(nq):
+                if 0 <= i + off < nk:
+                    _close(o[0, 0, i], v[0, 0, i + off], 1e-14, "window 0 picks the aligned key")
 
 
 # --------------------------------------------------------------------------
@@ -684,6 +729,7 @@ PINS = [
     pin_tile_size_invariance,
     pin_library_sdpa,
     pin_sampled_rows,
+    pin_mask_variants,
     pin_bwd_autograd,
     pin_bwd_finite_differences,
     pin_bwd_invariants,

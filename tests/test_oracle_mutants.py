@@ -23,11 +23,11 @@ ORACLE_DIR = pathlib.Path(__file__).resolve().parent.parent / "oracle"
 MUTANTS = [
     # --- dense definition -------------------------------------------------
     ("top_left_causal", "dense.py",
-     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j <= row_ids[:, None]"),
+     "ok &= j <= pos\n", "ok &= j <= row_ids[:, None]\n"),
     ("strict_causal", "dense.py",
-     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j < (row_ids[:, None] + (nk - nq))"),
+     "ok &= j <= pos\n", "ok &= j < pos\n"),
     ("causal_offset_sign", "dense.py",
-     "ok &= j <= (row_ids[:, None] + (nk - nq))", "ok &= j <= (row_ids[:, None] + (nq - nk))"),
+     "((nk - nq) if align", "((nq - nk) if align"),
     ("klen_off_by_one", "dense.py",
      "ok = np.broadcast_to(j < limit,", "ok = np.broadcast_to(j <= limit,"),
     ("klen_ignored", "dense.py",
@@ -68,8 +68,8 @@ MUTANTS = [
     ("keys_reversed", "dense.py",
      "s = (q @ k.T) * float(scale)", "s = (q @ k[::-1].T) * float(scale)"),
     ("row_ids_ignored", "dense.py",
-     "ok = allowed_mask(row_ids, nq, nk, causal, k_len_b)",
-     "ok = allowed_mask(np.arange(rows), nq, nk, causal, k_len_b)"),
+     "ok = allowed_mask(row_ids, nq, nk, causal, k_len_b,",
+     "ok = allowed_mask(np.arange(rows), nq, nk, causal, k_len_b,"),
     # --- tile recurrence and merge ------------------------------------------
     ("rescale_l_only", "online.py",
      "u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]", "u[r] = u[r] + e @ v[ka:kb][ok[r]]"),
@@ -103,6 +103,16 @@ MUTANTS = [
      "e = np.exp(x - m)\n    return m, e.sum(), e @ vals", "e = np.exp(x)\n    return m, e.sum(), e @ vals"),
     ("block_state_normalised", "online.py",
      "return m, e.sum(), e @ vals", "return m, e.sum(), (e @ vals) / e.sum()"),
+    # --- mask variants ------------------------------------------------------
+    ("top_left_offset", "dense.py",
+     "pos = row_ids[:, None] + ((nk - nq) if align == \"bottom_right\" else 0)",
+     "pos = row_ids[:, None] + (nk - nq)"),
+    ("window_left_off_by_one", "dense.py",
+     "ok &= j >= pos - int(wl)", "ok &= j > pos - int(wl)"),
+    ("window_left_sign", "dense.py",
+     "ok &= j >= pos - int(wl)", "ok &= j >= pos + int(wl)"),
+    ("window_right_ignored", "dense.py",
+     "ok &= j <= pos + int(wr)", "ok &= j <= pos + nk"),
     # --- backward by recomputation ------------------------------------------
     ("bwd_c_dropped", "backward.py",
      "d = p * (g @ v.T - c[:, None])", "d = p * (g @ v.T)"),
