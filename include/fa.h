@@ -57,7 +57,8 @@ typedef enum {
   FA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
                              or too large for 32-bit grid/index arithmetic   */
   FA_ERR_UNSUPPORTED = 3, /* dtype, head dim (> 128), block_n, chunk, causal
-                             flag or scale outside what the kernels support  */
+                             flag, alignment, window width or scale outside
+                             what the kernels support                        */
   FA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small     */
   FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
 } fa_status;
@@ -93,6 +94,47 @@ int fa_check_fwd(const void* q, const void* k, const void* v,
                  const float* bias, const int32_t* k_len, const void* o,
                  const float* lse, int B, int H, int Nq, int Nk, int dk,
                  int dv, int dtype, float scale, int causal, int block_n);
+
+/* Where query row i sits on the key axis ([GS] section 6): with the ENDS of
+ * the two sequences aligned (bottom-right, the convention since
+ * FlashAttention 2.1) at position i + Nk - Nq; with their STARTS aligned
+ * (top-left, the earlier convention) at position i. */
+typedef enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 } fa_align;
+
+/*
+ * fa_fwd_ex -- fa_fwd with the mask variants of [GS] section 6: a causal
+ * alignment choice and a sliding window measured from the same aligned
+ * position.  Arguments as for fa_fwd, plus
+ *
+ *   align        FA_ALIGN_BOTTOM_RIGHT or FA_ALIGN_TOP_LEFT; the row's key
+ *                position is pos_i = i + Nk - Nq or pos_i = i.  It applies
+ *                to the causal mask and to both window edges.
+ *   window_left  -1 (no left edge) or w >= 0: keys j >= pos_i - w only
+ *   window_right -1 (no right edge) or w >= 0: keys j <= pos_i + w only
+ *
+ * J_i = { j : j < clamp(k_len[b], 0, Nk), j <= pos_i if causal,
+ *             j >= pos_i - window_left if window_left >= 0,
+ *             j <= pos_i + window_right if window_right >= 0 }.
+ * The usual sliding window of width W is causal = 1, window_left = W - 1.
+ * Rows whose J_i is empty (a window entirely past k_len, or before key 0)
+ * get o_i = 0, lse_i = -inf.  With align = BOTTOM_RIGHT and both widths -1
+ * the result equals fa_fwd's bit for bit.  Any other mask runs on the
+ * general kernels (both dtypes), which skip the key tiles outside the union
+ * of a row block's ranges.
+ * Returns FA_ERR_UNSUPPORTED for another align value or a width below -1.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias,
+              const int32_t* k_len, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int dk, int dv, int dtype, float scale,
+              int causal, int align, int window_left, int window_right,
+              int block_n, void* stream);
+
+/* Host-only validation of fa_fwd_ex's arguments. */
+int fa_check_fwd_ex(const void* q, const void* k, const void* v,
+                    const float* bias, const int32_t* k_len, const void* o,
+                    const float* lse, int B, int H, int Nq, int Nk, int dk,
+                    int dv, int dtype, float scale, int causal, int align,
+                    int window_left, int window_right, int block_n);
 
 /*
  * Bytes of fp32 workspace fa_decode_splitk needs:

@@ -6,9 +6,9 @@ pointers and torch's current HIP stream to the C ABI (include/fa.h).  Every
 step of the computation runs in the library's HIP kernels; there is no CPU
 or PyTorch fallback.  If libfa.so is missing, every call raises.
 
-The names match the C entry points: fa_fwd, fa_decode_splitk,
-fa_decode_splitk_workspace_bytes, fa_check_fwd, fa_check_decode,
-fa_status_str, fa_abi_version.
+The names match the C entry points (fa_fwd, fa_fwd_ex, fa_decode_splitk,
+fa_decode_splitk_mq, fa_bwd, their workspace-size and fa_check_* companions,
+fa_status_str, fa_abi_version).
 """
 
 import ctypes
@@ -23,14 +23,18 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_BF16", "FaError", "lib", "lib_path",
-    "fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
-    "fa_check_fwd", "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
+    "FA_ALIGN_BOTTOM_RIGHT", "FA_ALIGN_TOP_LEFT",
+    "fa_fwd", "fa_fwd_ex", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
+    "fa_check_fwd", "fa_check_fwd_ex", "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
     "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes", "fa_check_decode_mq",
     "fa_status_str", "fa_abi_version",
 ]
 
 FA_F32 = 0
 FA_BF16 = 1
+FA_ALIGN_BOTTOM_RIGHT = 0
+FA_ALIGN_TOP_LEFT = 1
+_ALIGN = {"bottom_right": FA_ALIGN_BOTTOM_RIGHT, "top_left": FA_ALIGN_TOP_LEFT}
 _STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
            4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
 
@@ -43,6 +47,10 @@ _i, _f, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_check_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i]),
+    "fa_fwd_ex": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i,
+                       _vp]),
+    "fa_check_fwd_ex": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i,
+                             _i]),
     "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
@@ -116,6 +124,13 @@ def fa_check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scal
                               int(causal), block_n)
 
 
+def fa_check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align,
+                    window_left, window_right, block_n):
+    """Host-only validation of fa_fwd_ex; pointers are plain integers (or None)."""
+    return lib().fa_check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale,
+                                 int(causal), int(align), int(window_left), int(window_right), block_n)
+
+
 def fa_check_decode(q, k, v, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, workspace,
                     workspace_bytes):
     return lib().fa_check_decode(q, k, v, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale,
@@ -157,10 +172,7 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def fa_fwd(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, block_n=0, out=None, lse=None,
-           want_lse=True):
-    """Attention forward: q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv] (bf16 or fp32),
-    bias fp32 [B,H,Nq,Nk] or None, k_len int32 [B] or None.  Returns (o, lse)."""
+def _fwd_prepare(q, k, v, bias, k_len, scale, out, lse, want_lse):
     _need(q, "q", dims=4)
     dev = q.device
     _need(k, "k", dtype=q.dtype, dims=4, device=dev)
@@ -191,9 +203,36 @@ def fa_fwd(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, block_n=
         _need(lse, "lse", dtype=torch.float32, dims=3, device=dev)
         if tuple(lse.shape) != (B, H, Nq):
             raise FaError(2, "lse has the wrong shape")
+    return (B, H, Nq, Nk, dk, dv), float(scale), out, lse
+
+
+def fa_fwd(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, block_n=0, out=None, lse=None,
+           want_lse=True):
+    """Attention forward: q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv] (bf16 or fp32),
+    bias fp32 [B,H,Nq,Nk] or None, k_len int32 [B] or None.  Returns (o, lse)."""
+    dims, scale, out, lse = _fwd_prepare(q, k, v, bias, k_len, scale, out, lse, want_lse)
     st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(k_len), _ptr(out), _ptr(lse),
-                      B, H, Nq, Nk, dk, dv, _dtype_code(q), float(scale), int(bool(causal)), int(block_n),
-                      _stream(dev))
+                      *dims, _dtype_code(q), scale, int(bool(causal)), int(block_n), _stream(q.device))
+    if st != 0:
+        raise FaError(st)
+    return out, lse
+
+
+def fa_fwd_ex(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, align="bottom_right",
+              window_left=None, window_right=None, block_n=0, out=None, lse=None, want_lse=True):
+    """fa_fwd with the mask variants: ``align`` "bottom_right" (row i at key
+    position i + Nk - Nq) or "top_left" (at position i); ``window_left`` /
+    ``window_right`` None (open) or a width w >= 0 around that position."""
+    if align not in _ALIGN:
+        raise FaError(3, f"align must be one of {sorted(_ALIGN)}, got {align!r}")
+    wl = -1 if window_left is None else int(window_left)
+    wr = -1 if window_right is None else int(window_right)
+    if wl < 0 and window_left is not None or wr < 0 and window_right is not None:
+        raise FaError(3, "window widths must be None or >= 0")
+    dims, scale, out, lse = _fwd_prepare(q, k, v, bias, k_len, scale, out, lse, want_lse)
+    st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(k_len), _ptr(out), _ptr(lse),
+                         *dims, _dtype_code(q), scale, int(bool(causal)), _ALIGN[align], wl, wr, int(block_n),
+                         _stream(q.device))
     if st != 0:
         raise FaError(st)
     return out, lse

@@ -54,6 +54,39 @@ int check_fwd(const void* q, const void* k, const void* v, const float* bias, co
   return FA_OK;
 }
 
+int check_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+                 const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
+                 float scale, int causal, int align, int window_left, int window_right, int block_n) {
+  if (align != FA_ALIGN_BOTTOM_RIGHT && align != FA_ALIGN_TOP_LEFT) return FA_ERR_UNSUPPORTED;
+  if (window_left < -1 || window_right < -1) return FA_ERR_UNSUPPORTED;
+  return check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n);
+}
+
+// Forward arguments with the position masks folded into (off, wl, wr):
+// causal is the right width 0, which is also the narrowest right window.
+fa::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+                          void* o, float* lse, int B, int H, int Nq, int Nk, int dk, int dv, float scale,
+                          int causal, int align, int window_left, int window_right, int block_n) {
+  const int off = align == FA_ALIGN_BOTTOM_RIGHT ? Nk - Nq : 0;
+  const int wr = causal ? 0 : window_right;
+  const bool plain = window_left < 0 && (wr < 0 || (wr == 0 && off == Nk - Nq));
+  fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, plain ? (wr == 0 ? 1 : 0) : -1,
+                block_n == 0 ? 64 : block_n, off, window_left, wr};
+  return a;
+}
+
+int launch_fwd(const fa::FwdArgs& a, int dtype, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  // the fast bf16 kernel knows only the plain masks (none, or bottom-right
+  // causal); causal = -1 marks anything else
+  if (dtype == FA_BF16)
+    e = (a.causal >= 0 && fa::fwd_bf16_fast_eligible(a)) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
+  else
+    e = fa::launch_fwd_f32(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int check_decode(const void* q, const void* k, const void* v, const int32_t* k_len, const void* o,
                  const float* lse, int B, int H, int Nk, int dk, int dv, int chunk, int dtype, float scale,
                  const void* workspace, size_t workspace_bytes) {
@@ -134,14 +167,14 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 extern "C" {
 
-int fa_abi_version(void) { return 102; }
+int fa_abi_version(void) { return 103; }
 
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large shape";
-    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block_n, chunk, causal flag or scale";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block_n, chunk, causal flag, alignment, window or scale";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
@@ -160,14 +193,28 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, const
   const int st = check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n);
   if (st != FA_OK) return st;
   if ((long long)B * H * Nq == 0) return FA_OK;
-  fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal, block_n == 0 ? 64 : block_n};
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == FA_BF16)
-    e = fa::fwd_bf16_fast_eligible(a) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
-  else
-    e = fa::launch_fwd_f32(a, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launch_fwd(make_fwd_args(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal,
+                                  FA_ALIGN_BOTTOM_RIGHT, -1, -1, block_n),
+                    dtype, stream);
+}
+
+int fa_check_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+                    const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
+                    float scale, int causal, int align, int window_left, int window_right, int block_n) {
+  return check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align, window_left,
+                      window_right, block_n);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len, void* o,
+              float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype, float scale, int causal,
+              int align, int window_left, int window_right, int block_n, void* stream) {
+  const int st = check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align,
+                              window_left, window_right, block_n);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  return launch_fwd(make_fwd_args(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal, align,
+                                  window_left, window_right, block_n),
+                    dtype, stream);
 }
 
 size_t fa_decode_splitk_workspace_bytes(int B, int H, int Nk_max, int dv, int chunk) {

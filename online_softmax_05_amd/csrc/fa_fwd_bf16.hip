@@ -37,7 +37,14 @@
 // -inf, the exponent origin used is 0, every p is exp2(-inf) = 0 and
 // alpha = 0 multiplies zeros, so exp(-inf - (-inf)) is never formed
 // ([GS] section 6).
+//
+// Position masks (causal in either alignment, sliding windows) come as a
+// visible key range [lo, end) per row whose ends grow with the row; the
+// work-group visits only the key tiles that meet the union of its rows'
+// ranges, and only tiles not inside every row's range of a wave are masked
+// element by element ([GS] section 6).
 #include "fa_common.h"
+#include "fa_mask.h"
 #include "launch.h"
 
 namespace fa {
@@ -149,18 +156,18 @@ template <int DK, int DV, int BN, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, int causal,
+    float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, KeyRange mr,
     int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
   using T = Tile<DK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31;  // query row within the wave / MFMA column
   const int hf = lane >> 5;   // lane half
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, causal != 0);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, mr.wr >= 0);
   const int b = tc.bh / H;
   const int q0 = tc.qt * kBM;
   const int klen = clamp_klen(k_len, b, Nk);
@@ -172,14 +179,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const uint16_t* kbh = k + bh * Nk * dk;
   const uint16_t* vbh = v + bh * Nk * dv;
 
-  // keys this row may see are [0, row_end); row_end <= 0 means an empty row
-  const int shift = Nk - Nq;
-  const int row_end = causal ? min(klen, qi + shift + 1) : klen;
+  // keys this row may see are [row_lo, row_end) (empty when row_lo >=
+  // row_end); tiles inside [wave_max_lo, wave_min_end) need no per-element
+  // mask for this wave
+  const int row_lo = key_lo(mr, qi);
+  const int row_end = key_end(mr, qi, klen);
+  const unsigned row_span = row_end > row_lo ? (unsigned)(row_end - row_lo) : 0u;
   const int wave_first = q0 + wave * 32;
-  const int wave_min_end = causal ? min(klen, wave_first + shift + 1) : klen;
-  const int last_row = min(q0 + kBM, Nq) - 1;
-  const int kend = visible_key_end(klen, causal != 0, last_row, Nq, Nk);
-  const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int wave_max_lo = key_lo(mr, wave_first + 31);
+  const int wave_min_end = key_end(mr, wave_first, klen);
+  const int kbeg = key_lo(mr, q0);
+  const int kend = key_end(mr, min(q0 + kBM, Nq) - 1, klen);
+  const int t_begin = kbeg / BN;
+  const int t_end = kend > kbeg ? (kend + BN - 1) / BN : t_begin;
 
   // Logit scale in the base-2 domain, made positive: a negative scale flips
   // the sign of Q instead (exact in bf16), and a zero scale is replaced by a
@@ -210,19 +222,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   float l_run = 0.f;      // this lane half's part of the running denominator
 
   Prefetch<DK, DV, BN> pf;
-  if (n_tiles > 0) {
-    fetch_tile<DK, DV, BN>(pf, kbh, vbh, 0, Nk, dk, dv, vec_k != 0, vec_v != 0, tid);
-    store_tile<DK, DV, BN>(pf, smem, tid);
+  if (t_begin < t_end) {
+    fetch_tile<DK, DV, BN>(pf, kbh, vbh, t_begin * BN, Nk, dk, dv, vec_k != 0, vec_v != 0, tid);
+    store_tile<DK, DV, BN>(pf, smem + (t_begin & 1) * T::BUF, tid);
   }
   __syncthreads();
 
   const float* brow = BIAS ? bias + (bh * Nq + (size_t)(row_valid ? qi : 0)) * Nk : nullptr;
 
-  for (int it = 0; it < n_tiles; ++it) {
+  for (int it = t_begin; it < t_end; ++it) {
     const int n0 = it * BN;
     const uint16_t* ks = smem + (it & 1) * T::BUF;
     const uint16_t* vt = ks + T::K_ELEMS;
-    const bool has_next = it + 1 < n_tiles;
+    const bool has_next = it + 1 < t_end;
     if (has_next) fetch_tile<DK, DV, BN>(pf, kbh, vbh, n0 + BN, Nk, dk, dv, vec_k != 0, vec_v != 0, tid);
 
     // ---- S^T = K Q^T for this wave's 32 rows and BN keys ----------------
@@ -245,26 +257,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // With a bias s[] keeps c s and the biased logit only feeds the maximum;
     // the exponent re-adds the bias after subtracting the maximum, so large
     // bias values cancel before rounding.
-    const bool need_mask = n0 + BN > wave_min_end;
+    //
+    // The mask is one unsigned range test and a select per element, under a
+    // wave-uniform branch: a short-circuit condition here was compiled into
+    // per-element exec-mask diamonds that lost unmasked values.
+    if (n0 < wave_max_lo || n0 + BN > wave_min_end) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+          const bool vis = (unsigned)(key - row_lo) < row_span;
+          s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key0 = n0 + kb * 32 + 8 * i + 4 * hf;
         f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-        if (BIAS) bv = load_bias4(brow, key0, Nk, vec_bias != 0, row_valid);
+        if (BIAS) bv = load_bias4(brow, n0 + kb * 32 + 8 * i + 4 * hf, Nk, vec_bias != 0, row_valid);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool masked = need_mask && key0 + j >= row_end;
           if (BIAS) {
-            const float sc = masked ? kNegInf : s[kb][4 * i + j] * c;
+            const float sc = s[kb][4 * i + j] * c;  // -inf stays -inf (c > 0)
             s[kb][4 * i + j] = sc;
             mx = fmaxf(mx, sc + bv[j] * kLog2e);
           } else {
-            const float x = masked ? kNegInf : s[kb][4 * i + j];
-            s[kb][4 * i + j] = x;
-            mx = fmaxf(mx, x);
+            mx = fmaxf(mx, s[kb][4 * i + j]);
           }
         }
       }
@@ -379,7 +400,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & mask16) == 0);
   hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, BN, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
-                     (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e, a.causal,
+                     (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e,
+                     KeyRange{a.off, a.wl, a.wr},
                      (int)vec_q, (int)vec_k, (int)vec_v, (int)vec_b, n_qt);
   return hipGetLastError();
 }

@@ -16,7 +16,14 @@
 // lane half per k-step, V can stay row-major in LDS.  The tile is staged
 // through a single LDS buffer: these shapes are small and this kernel
 // favours plainness over overlap.
+//
+// Position masks (causal in either alignment, sliding windows) come as a
+// visible key range [lo, end) per row whose ends grow with the row; the
+// work-group visits only the key tiles that meet the union of its rows'
+// ranges, and only tiles not inside every row's range of a wave are masked
+// element by element ([GS] section 6).
 #include "fa_common.h"
+#include "fa_mask.h"
 #include "launch.h"
 
 namespace fa {
@@ -50,7 +57,7 @@ template <int DK, int DV, int BN, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, float* __restrict__ o,
-    float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, int causal,
+    float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, KeyRange mr,
     int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
   using T = TileF<DK, DV, BN>;
   __shared__ __attribute__((aligned(16))) float smem[T::K_ELEMS + T::V_ELEMS];
@@ -59,11 +66,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int hf = lane >> 5;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, causal != 0);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, mr.wr >= 0);
   const int b = tc.bh / H;
   const int q0 = tc.qt * kBM;
   const int klen = clamp_klen(k_len, b, Nk);
@@ -74,11 +81,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   const float* kbh = k + bh * Nk * dk;
   const float* vbh = v + bh * Nk * dv;
 
-  const int shift = Nk - Nq;
-  const int row_end = causal ? min(klen, qi + shift + 1) : klen;
-  const int wave_min_end = causal ? min(klen, q0 + wave * 32 + shift + 1) : klen;
-  const int kend = visible_key_end(klen, causal != 0, min(q0 + kBM, Nq) - 1, Nq, Nk);
-  const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // keys this row may see are [row_lo, row_end); tiles inside
+  // [wave_max_lo, wave_min_end) need no per-element mask for this wave
+  const int row_lo = key_lo(mr, qi);
+  const int row_end = key_end(mr, qi, klen);
+  const unsigned row_span = row_end > row_lo ? (unsigned)(row_end - row_lo) : 0u;
+  const int wave_first = q0 + wave * 32;
+  const int wave_max_lo = key_lo(mr, wave_first + 31);
+  const int wave_min_end = key_end(mr, wave_first, klen);
+  const int kbeg = key_lo(mr, q0);
+  const int kend = key_end(mr, min(q0 + kBM, Nq) - 1, klen);
+  const int t_begin = kbeg / BN;
+  const int t_end = kend > kbeg ? (kend + BN - 1) / BN : t_begin;
 
   // Q^T fragment: k-step t holds dim 2t + half of row qi
   float qf[DK / 2];
@@ -100,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   float l_run = 0.f;
   const float* brow = BIAS ? bias + (bh * Nq + (size_t)(row_valid ? qi : 0)) * Nk : nullptr;
 
-  for (int it = 0; it < n_tiles; ++it) {
+  for (int it = t_begin; it < t_end; ++it) {
     const int n0 = it * BN;
     __syncthreads();  // the previous tile has been consumed by every wave
     for (int id = tid; id < BN * DK / 4; id += kThreads) {
@@ -131,27 +145,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
       }
     }
 
-    // scale (+ bias) and mask in the base-2 domain
-    const bool need_mask = n0 + BN > wave_min_end;
+    // scale into the base-2 domain, then mask: one unsigned range test and
+    // a select per element, under a wave-uniform branch (masking after the
+    // scale keeps -inf for any sign of the scale)
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] *= scale_log2;
+    if (n0 < wave_max_lo || n0 + BN > wave_min_end) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + kb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+          const bool vis = (unsigned)(key - row_lo) < row_span;
+          s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+    }
+    // s[] keeps scale*log2e*(q.k) (or -inf); with a bias the biased logit
+    // only feeds the maximum, and the exponent below re-adds the bias after
+    // subtracting the maximum, so large bias values cancel before rounding
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key0 = n0 + kb * 32 + 8 * i + 4 * hf;
         f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-        if (BIAS) bv = load_bias4(brow, key0, Nk, vec_bias != 0, row_valid);
+        if (BIAS) bv = load_bias4(brow, n0 + kb * 32 + 8 * i + 4 * hf, Nk, vec_bias != 0, row_valid);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // s[] keeps scale*log2e*(q.k) (or -inf); with a bias the biased
-          // logit only feeds the maximum, and the exponent below re-adds the
-          // bias after subtracting the maximum, so large bias values cancel
-          // before rounding
-          const bool masked = need_mask && key0 + j >= row_end;
-          const float sc = masked ? kNegInf : s[kb][4 * i + j] * scale_log2;
-          s[kb][4 * i + j] = sc;
-          mx = fmaxf(mx, BIAS ? sc + bv[j] * kLog2e : sc);
-        }
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, BIAS ? s[kb][4 * i + j] + bv[j] * kLog2e : s[kb][4 * i + j]);
       }
     }
     mx = half_swap_max(mx);
@@ -236,7 +258,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & m16) == 0);
   hipLaunchKernelGGL((fwd_f32_kernel<DK, DV, BN, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, a.bias, a.k_len, (float*)a.o,
-                     a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e, a.causal, (int)vec_q, (int)vec_k,
+                     a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr}, (int)vec_q, (int)vec_k,
                      (int)vec_v, (int)vec_b, n_qt);
   return hipGetLastError();
 }

@@ -34,7 +34,9 @@ def oracle_full(inp):
     """Dense oracle over a whole (small) workload dict of CPU or device tensors."""
     k_len = None if inp.get("k_len") is None else inp["k_len"].cpu().numpy()
     return oracle.attention_ref(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale=scale32(inp["scale"]),
-                                causal=inp["causal"], k_len=k_len, bias=f64(inp.get("bias")))
+                                causal=inp["causal"], k_len=k_len, bias=f64(inp.get("bias")),
+                                align=inp.get("align", "bottom_right"),
+                                window=(inp.get("window_left"), inp.get("window_right")))
 
 
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None, logit_scale=1.0):
@@ -65,7 +67,8 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None, logit_scale
     return err_o, err_l
 
 
-def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None):
+def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None, align="bottom_right",
+                window=(None, None)):
     """Oracle on sampled rows of device tensors: rows is a list of (b, h, i).
     Only the needed slices are copied to the host.  Returns (o [n, dv], lse [n])."""
     B, H, Nq, _ = q.shape
@@ -82,7 +85,8 @@ def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None):
         kk, vv = f64(k[b, h]), f64(v[b, h])
         bb = None if bias is None else f64(bias[b, h, idx])
         ob, lb = oracle.attention_head(qi, kk, vv, scale=scale32(scale), nq=Nq, causal=causal,
-                                       k_len_b=None if kl is None else int(kl[b]), bias=bb, row_ids=idx)
+                                       k_len_b=None if kl is None else int(kl[b]), bias=bb, row_ids=idx,
+                                       align=align, window=window)
         for j, (n, _) in enumerate(items):
             o[n] = ob[j]
             lse[n] = lb[j]

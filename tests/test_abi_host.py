@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert {"fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes", "fa_check_fwd",
             "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd", "fa_status_str",
             "fa_abi_version", "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes",
-            "fa_check_decode_mq"} <= set(names)
+            "fa_check_decode_mq", "fa_fwd_ex", "fa_check_fwd_ex"} <= set(names)
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
@@ -60,7 +60,7 @@ def test_header_is_plain_c():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 102
+    assert fa.fa_abi_version() == 103
     for st in range(6):
         assert isinstance(fa.fa_status_str(st), str) and fa.fa_status_str(st)
     assert fa.fa_status_str(0) == "ok"
@@ -104,6 +104,34 @@ def check_fwd(**kw):
 ])
 def test_check_fwd(kw, want):
     assert check_fwd(**kw) == want
+
+
+def check_fwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, **kw):
+    a = fwd_args(**kw)
+    return fa.fa_check_fwd_ex(a["q"], a["k"], a["v"], a["bias"], a["k_len"], a["o"], a["lse"], a["B"],
+                              a["H"], a["Nq"], a["Nk"], a["dk"], a["dv"], a["dtype"], a["scale"], a["causal"],
+                              align, wl, wr, a["block_n"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, OK), ({"align": fa.FA_ALIGN_TOP_LEFT}, OK), ({"align": 2}, UNSUP), ({"align": -1}, UNSUP),
+    ({"wl": 0}, OK), ({"wr": 0}, OK), ({"wl": 127, "wr": 3, "causal": 0}, OK), ({"wl": 2**31 - 1}, OK),
+    ({"wl": -2}, UNSUP), ({"wr": -7}, UNSUP),
+    ({"wl": 4, "dk": 300}, UNSUP), ({"wl": 4, "q": None}, NULL), ({"wl": 4, "causal": 3}, UNSUP),
+    ({"wl": 4, "Nq": 0, "q": None, "o": None}, OK),
+])
+def test_check_fwd_ex(kw, want):
+    assert check_fwd_ex(**kw) == want
+
+
+def test_fwd_ex_rejects_before_launch():
+    st = fa.lib().fa_fwd_ex(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 5, -1, -1, 0, None)
+    assert st == UNSUP
+    st = fa.lib().fa_fwd_ex(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 0, -3, -1, 0, None)
+    assert st == UNSUP
+    st = fa.lib().fa_fwd_ex(None, None, None, None, None, None, None, 0, 4, 4, 4, 8, 8, fa.FA_F32, 1.0, 0, 1, 3,
+                            3, 0, None)
+    assert st == OK
 
 
 def test_fwd_rejects_before_launch():

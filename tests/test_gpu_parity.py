@@ -188,6 +188,27 @@ def _sweep_cases():
     return cases
 
 
+GENERAL_MULTI_TILE = [
+    # (Nq, Nk, dk, dv, causal, block_n): no bias, several key tiles, block
+    # widths the fast bf16 kernel does not take, so the general kernels run
+    (200, 200, 64, 64, True, 32), (200, 200, 64, 64, False, 32), (64, 200, 64, 64, False, 128),
+    (333, 517, 128, 128, True, 128), (517, 333, 128, 96, True, 32), (130, 700, 32, 64, False, 32),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_MULTI_TILE, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_general_kernels_no_bias_multi_tile(dev, case, dt):
+    """Regression: the no-bias general kernels over several key tiles, with
+    masked elements in the first accumulator slot of a tile."""
+    nq, nk, dk, dv, causal, bn = case
+    inp = workloads.seeded_case(6000 + nq + nk, 2, 2, nq, nk, dk, dv, DT[dt], causal=causal)
+    say(f"general no-bias multi-tile {case} {dt}")
+    o, lse = run_fwd(inp, dev, block_n=bn)
+    o_ref, lse_ref = oracle_full(inp)
+    compare(o, lse, o_ref, lse_ref, DT[dt], f"general no-bias {case} {dt}")
+
+
 @pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"s{c[0]}")
 def test_seeded_sweep(dev, case):
     n, B, H, nq, nk, dk, dv, dt, causal, bias, kl, bn = case
