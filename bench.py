@@ -1,11 +1,12 @@
 """Benchmark of the attention forward library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload prefill|long|decode|decode_mq|backward|window]
                     [--no-cpu-baseline] [--only] [--copy-calibration]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in device memory: one fa_fwd call for the prefill and
-long-context workloads, one fa_decode_splitk call (partial + merge kernels)
+long-context workloads, one fa_fwd_ex call for the sliding-window prefill, one fa_decode_splitk call (partial + merge kernels)
 for decode, one fa_decode_splitk_mq call for the multi-query decode, one
 fa_bwd call (dQ then dK/dV kernels; O and lse from one untimed fa_fwd) for
 the backward workload.  W untimed steps, then exactly K timed steps between device
@@ -14,7 +15,8 @@ synchronisations; the JSON line on stdout reports the main workload
 the long-context and decode workloads measured the same way.
 
 Algorithmic work (what the method must do, not what a kernel happens to do):
-* prefill / long: FLOPs = 2 (dk + dv) x (number of allowed query-key pairs);
+* prefill / long / window: FLOPs = 2 (dk + dv) x (number of allowed
+  query-key pairs, under the window for the sliding-window workload);
   exponentials and maxima are not counted;
 * backward: FLOPs = 2 (3 dk + 2 dv) x (allowed pairs): the five products
   S = QK^T, dP = G V^T, dV = P^T G, dK = D^T Q, dQ = D K ([GS] section 7);
@@ -53,8 +55,12 @@ METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s (% peak)"
 # sources of the kernel each workload's roofline describes (stored counter
 # summaries are only reported while these still hash to the recorded value)
 KERNEL_SOURCES = {
-    "prefill": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
-    "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+    "prefill": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
+                "online_softmax_05_amd/csrc/fa_mask.h"],
+    "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
+             "online_softmax_05_amd/csrc/fa_mask.h"],
+    "window": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
+               "online_softmax_05_amd/csrc/fa_mask.h"],
     "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "backward": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
                  "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h"],
@@ -62,6 +68,7 @@ KERNEL_SOURCES = {
                   "online_softmax_05_amd/csrc/fa_common.h"],
 }
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
+                "window": "fwd_bf16_fast_kernel<128, 128, false>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
                 "backward": "bwd_dq_bf16_kernel<128, 128, false> + bwd_dkdv_bf16_kernel<128, 128, false>",
                 "decode_mq": "mq_partial_bf16_kernel + mq_merge_kernel"}
@@ -78,11 +85,15 @@ def kernel_source_hash(name):
     return h.hexdigest()[:16]
 
 
-def causal_pairs(nq, nk):
-    """Allowed (query, key) pairs of one head under bottom-right causal."""
+def causal_pairs(nq, nk, window_left=None):
+    """Allowed (query, key) pairs of one head under bottom-right causal,
+    optionally limited to a left window of ``window_left`` keys before the
+    row's own position."""
     total = 0
     for i in range(nq):
-        total += max(0, min(nk, i + nk - nq + 1))
+        end = max(0, min(nk, i + nk - nq + 1))
+        lo = 0 if window_left is None else max(0, i + nk - nq - window_left)
+        total += max(0, end - lo)
     return total
 
 
@@ -145,6 +156,7 @@ def cpu_baseline_prefill(inp, name, budget_s):
     B, H, N, dk = q.shape
     dv = v.shape[3]
     scale = float(np.float32(inp["scale"]))
+    wl = inp.get("window_left")
     flops = 0.0
     heads = 0
     elapsed = 0.0  # oracle time only; device-to-host copies of the inputs are excluded
@@ -157,9 +169,9 @@ def cpu_baseline_prefill(inp, name, budget_s):
         for r0 in range(0, N, 2048):
             r1 = min(N, r0 + 2048)
             oracle.attention_head(qh[r0:r1], kh, vh, scale=scale, nq=N, causal=True,
-                                  row_ids=np.arange(r0, r1))
+                                  row_ids=np.arange(r0, r1), window=(wl, None))
         elapsed += time.perf_counter() - ts
-        flops += 2.0 * (dk + dv) * causal_pairs(N, N)
+        flops += 2.0 * (dk + dv) * causal_pairs(N, N, wl)
         heads += 1
         if elapsed >= budget_s:
             break
@@ -217,13 +229,19 @@ def run_prefill(name, args, dev):
     out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
+    wl = inp.get("window_left")
+
     def step():
-        fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"],
-                  out=out, lse=lse)
+        if wl is None:
+            fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"],
+                      out=out, lse=lse)
+        else:
+            fa.fa_fwd_ex(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, window_left=wl,
+                         block_n=inp["block_n"], out=out, lse=lse)
 
     log(f"{name}: timing {args.warmup} + {args.steps} steps")
     t = time_launches(step, args.steps, args.warmup)
-    pairs = B * H * causal_pairs(N, N)
+    pairs = B * H * causal_pairs(N, N, wl)
     flops = 2.0 * (dk + dv) * pairs
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -239,7 +257,7 @@ def run_prefill(name, args, dev):
                       + 4 * B * H * N),
         config=dict(workload=workloads.DESCRIPTIONS[name], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
                     dtype="bf16", block_n=64 if inp["block_n"] == 0 else inp["block_n"],
-                    allowed_pairs=pairs),
+                    allowed_pairs=pairs, **({} if wl is None else {"window_left": wl})),
     )
     if not args.no_cpu_baseline:
         log(f"{name}: timing the oracle on a bounded sample")
@@ -423,7 +441,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["prefill", "long", "decode", "decode_mq", "backward"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "decode", "decode_mq", "backward", "window"],
+                    default="prefill")
     ap.add_argument("--only", action="store_true", help="measure only the main workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -448,8 +467,8 @@ def main():
         copy_calibration(dev)
         return
 
-    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "decode_mq", "backward")
-                                                      if w != args.workload])
+    order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "decode_mq", "backward",
+                                                                  "window") if w != args.workload])
     runners = {"decode": run_decode, "decode_mq": run_decode_mq, "backward": run_backward}
     results = {}
     for w in order:

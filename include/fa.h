@@ -118,9 +118,9 @@ typedef enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 } fa_align;
  * The usual sliding window of width W is causal = 1, window_left = W - 1.
  * Rows whose J_i is empty (a window entirely past k_len, or before key 0)
  * get o_i = 0, lse_i = -inf.  With align = BOTTOM_RIGHT and both widths -1
- * the result equals fa_fwd's bit for bit.  Any other mask runs on the
- * general kernels (both dtypes), which skip the key tiles outside the union
- * of a row block's ranges.
+ * the result equals fa_fwd's bit for bit.  Every kernel (both dtypes, the
+ * bf16 head-dim 64/128 fast path included) visits only the key tiles that
+ * meet the union of a row block's ranges and masks only the edge tiles.
  * Returns FA_ERR_UNSUPPORTED for another align value or a width below -1.
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias,

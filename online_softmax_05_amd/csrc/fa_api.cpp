@@ -69,19 +69,16 @@ fa::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const flo
                           int causal, int align, int window_left, int window_right, int block_n) {
   const int off = align == FA_ALIGN_BOTTOM_RIGHT ? Nk - Nq : 0;
   const int wr = causal ? 0 : window_right;
-  const bool plain = window_left < 0 && (wr < 0 || (wr == 0 && off == Nk - Nq));
-  fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, plain ? (wr == 0 ? 1 : 0) : -1,
-                block_n == 0 ? 64 : block_n, off, window_left, wr};
+  fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, block_n == 0 ? 64 : block_n,
+                off, window_left, wr};
   return a;
 }
 
 int launch_fwd(const fa::FwdArgs& a, int dtype, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // the fast bf16 kernel knows only the plain masks (none, or bottom-right
-  // causal); causal = -1 marks anything else
   if (dtype == FA_BF16)
-    e = (a.causal >= 0 && fa::fwd_bf16_fast_eligible(a)) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
+    e = fa::fwd_bf16_fast_eligible(a) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
   else
     e = fa::launch_fwd_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

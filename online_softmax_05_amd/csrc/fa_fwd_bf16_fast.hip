@@ -42,6 +42,12 @@
 //   share each CU, so one wave's softmax (VALU) overlaps the other wave's
 //   matrix products on the same SIMD.  Tiles that need no mask for any row
 //   of the work-group run a variant without mask code.
+// * Position masks (causal in either alignment, sliding windows) arrive as a
+//   visible key range [lo, end) per row, both ends growing with the row
+//   ([GS] section 6).  A work-group visits the key tiles that meet the union
+//   of its rows' ranges: a masked run along the left window edge, unmasked
+//   tiles inside every row's range, then a masked run along the right edge
+//   (the causal diagonal, the key-length boundary).
 //
 // Online state per query row (base-2 domain): reference m (moved lazily,
 // only when the tile maximum exceeds it by more than 8), denominator l and
@@ -50,6 +56,7 @@
 // is divided once at the end ([GS] section 5).  Rows with no allowed key keep
 // m = -inf and produce o = 0, lse = -inf ([GS] section 6).
 #include "fa_common.h"
+#include "fa_mask.h"
 #include "launch.h"
 
 namespace fa {
@@ -264,7 +271,8 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&p
 // by; the return value says whether any row of the wave moved its reference.
 template <bool MASK, bool BIAS>
 __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2], RowState& st, float (&alpha)[2],
-                                             float c, int n0, const int (&row_end)[2], const float* const (&brow)[2],
+                                             float c, int n0, const int (&row_lo)[2],
+                                             const unsigned (&row_span)[2], const float* const (&brow)[2],
                                              const bool (&rvalid)[2], int nk, bool vec_bias, int g) {
   float xo[2][4][4];  // bias path: the raw bias per element
   float mx[2];
@@ -279,7 +287,7 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = s[kb][qb][j];
-        if (MASK && key0 + j >= row_end[qb]) x = kNegInf;
+        if (MASK && (unsigned)(key0 + j - row_lo[qb]) >= row_span[qb]) x = kNegInf;
         if (BIAS) {
           // keep c*s; the biased logit only feeds the maximum, and the
           // exponent adds bias*log2e - m in one rounding (large biases
@@ -339,9 +347,11 @@ struct FwdTile {
   // inputs of this work-group
   const uint16_t* kbh;
   const uint16_t* vbh;
-  int nk, n_tiles;
+  int nk, n_tiles;  // n_tiles: one past the last tile the work-group visits
   float c;
-  int row_end[2];
+  int qrow0;    // global index of this lane's row in query block 0 (block 1: +16)
+  int klen;     // keys of this sequence
+  KeyRange mr;  // position masks; row ranges are rebuilt only for masked tiles
   bool rvalid[2];
   const float* brow[2];
   int vec_bias, g;
@@ -364,10 +374,20 @@ struct FwdTile {
     }
     f32x4 s[4][2];
     qk_tile<DK, DV>(s, qf, kcur, la);
+    int row_lo[2] = {0, 0};
+    unsigned row_span[2] = {0u, 0u};
+    if (MASK) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int lo = key_lo(mr, qrow0 + 16 * qb), end = key_end(mr, qrow0 + 16 * qb, klen);
+        row_lo[qb] = lo;
+        row_span[qb] = end > lo ? (unsigned)(end - lo) : 0u;
+      }
+    }
     bf16x8 pb[2][2];
     float alpha[2];
     const bool grow =
-        softmax_tile<MASK, BIAS>(s, pb, st, alpha, c, n0, row_end, brow, rvalid, nk, vec_bias != 0, g);
+        softmax_tile<MASK, BIAS>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk, vec_bias != 0, g);
     if (grow) {
 #pragma unroll
       for (int d = 0; d < DV / 16; ++d) {
@@ -385,7 +405,7 @@ template <int DK, int DV, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int H, int Nq, int Nk, float scale_log2, int causal, int vec_bias, int n_qt) {
+    float* __restrict__ lse, int H, int Nq, int Nk, float scale_log2, KeyRange mr, int vec_bias, int n_qt) {
   __shared__ __attribute__((aligned(1024))) char kbuf0[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[SwzTile<DV>::BYTES];
@@ -403,9 +423,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   // Under a causal mask query tile i visits about i + 1 key tiles; a
   // work-group takes the pair (n_qt - 1 - u, u), heavy one first, so that
   // every work-group does the same work and the grid drains evenly.
-  const bool pair = causal != 0 && FA_FAST_PAIR;
+  const bool pair = FA_FAST_PAIR && mr.wl < 0 && mr.wr == 0;
   const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, causal != 0 && !pair);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, mr.wr >= 0 && !pair);
   const int n_pass = (pair && 2 * tc.qt + 1 != n_qt) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
   const int qt = pair ? (pass == 0 ? n_qt - 1 - tc.qt : tc.qt) : tc.qt;
@@ -423,18 +443,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   ft.g = g;
   ft.la.init(lane, wave);
 
-  const int shift = Nk - Nq;
   int qrow[2];
+  ft.qrow0 = q0 + wave * 32 + r16;
+  ft.klen = klen;
+  ft.mr = mr;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     qrow[qb] = q0 + wave * 32 + qb * 16 + r16;
     ft.rvalid[qb] = qrow[qb] < Nq;
-    ft.row_end[qb] = causal ? min(klen, qrow[qb] + shift + 1) : klen;
     ft.brow[qb] = BIAS ? bias + (bh * Nq + (size_t)(ft.rvalid[qb] ? qrow[qb] : 0)) * Nk : nullptr;
   }
-  const int kend = visible_key_end(klen, causal != 0, min(q0 + kBM, Nq) - 1, Nq, Nk);
-  const int n_tiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
-  ft.n_tiles = n_tiles;
+  // tiles [t_begin, t_end) meet some row's range; tiles [t_full, t_full_end)
+  // lie inside every row's range (the last row has the largest lo, the first
+  // row the smallest end)
+  const int last_row = min(q0 + kBM, Nq) - 1;
+  const int kbeg = key_lo(mr, q0);
+  const int kend = key_end(mr, last_row, klen);
+  const int t_begin = kbeg / kBN;
+  const int t_end = kend > kbeg ? (kend + kBN - 1) / kBN : t_begin;
+  ft.n_tiles = t_end;
 
   // logit scale in the base-2 domain, made positive (a negative scale flips
   // the sign of Q, exactly; zero becomes a tiny positive value)
@@ -461,29 +488,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   ft.st.m[0] = ft.st.m[1] = kNegInf;
   ft.st.l[0] = ft.st.l[1] = 0.f;
 
-  if (n_tiles > 0) {
-    load_tile<DK>(ft.kbh, Nk, ft.la.kld, K0, wave);
-    load_tile<DV>(ft.vbh, Nk, ft.la.vld, V0, wave);
+  if (t_begin < t_end) {
+    load_tile<DK>(ft.kbh + (size_t)t_begin * kBN * DK, Nk - t_begin * kBN, ft.la.kld, K0, wave);
+    load_tile<DV>(ft.vbh + (size_t)t_begin * kBN * DV, Nk - t_begin * kBN, ft.la.vld, V0, wave);
     wait_loads();
     __syncthreads();
 
-    // Tiles before the work-group's first row's visible end need no mask
-    // for any of its rows; the rest (the causal diagonal, the key-length
-    // boundary) run the masked variant.  Buffers alternate with the parity
-    // of the tile index.
-    const int wg_first_end = causal ? min(klen, q0 + shift + 1) : klen;
-    const int n_full = min(n_tiles, max(wg_first_end, 0) / kBN);
-    int t = 0;
-    for (; t + 1 < n_full; t += 2) {
+    // Tile t sits in buffer 0 or 1 by the parity of t - t_begin.  The
+    // unmasked run starts at an even distance from t_begin (a tile moved
+    // into the masked run is still computed correctly), so it always starts
+    // in buffer 0.
+    const int lo_last = key_lo(mr, last_row);
+    const int end_first = key_end(mr, q0, klen);
+    int t_full = min(max((lo_last + kBN - 1) / kBN, t_begin), t_end);
+    t_full = min(t_full + ((t_full - t_begin) & 1), t_end);
+    const int t_full_end = max(min(end_first / kBN, t_end), t_full);
+    int t = t_begin;
+    for (; t < t_full; ++t) {  // along the left window edge
+      if ((t - t_begin) & 1)
+        ft.template step<true>(t, wave, K1, V1, K0, V0);
+      else
+        ft.template step<true>(t, wave, K0, V0, K1, V1);
+    }
+    for (; t + 1 < t_full_end; t += 2) {
       ft.template step<false>(t, wave, K0, V0, K1, V1);
       ft.template step<false>(t + 1, wave, K1, V1, K0, V0);
     }
-    if (t < n_full) {
+    if (t < t_full_end) {
       ft.template step<false>(t, wave, K0, V0, K1, V1);
       ++t;
     }
-    for (; t < n_tiles; ++t) {
-      if (t & 1)
+    for (; t < t_end; ++t) {  // the diagonal / right edge and the key-length boundary
+      if ((t - t_begin) & 1)
         ft.template step<true>(t, wave, K1, V1, K0, V0);
       else
         ft.template step<true>(t, wave, K0, V0, K1, V1);
@@ -514,12 +550,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
 template <int DK, int DV, bool BIAS>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
-  const int n_units = (a.causal && FA_FAST_PAIR) ? (n_qt + 1) / 2 : n_qt;
+  const bool pair = FA_FAST_PAIR && a.wl < 0 && a.wr == 0;
+  const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
   const long long total = (long long)n_units * a.H * a.B;
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & 15) == 0);
   hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
-                     (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.scale * kLog2e, a.causal, (int)vec_b, n_qt);
+                     (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr},
+                     (int)vec_b, n_qt);
   return hipGetLastError();
 }
 

@@ -17,11 +17,10 @@ struct FwdArgs {
   float* lse;
   int B, H, Nq, Nk, dk, dv;
   float scale;
-  int causal;   // bottom-right causal and no window (the fast kernel's only mask)
   int block_n;  // 32, 64 or 128 (already resolved from "auto")
-  // position masks of the general kernels, see fa_mask.h: row i sits at key
-  // position i + off and sees keys [pos - wl, pos + wr] (a negative width is
-  // unbounded; causal is folded into wr)
+  // position masks, see fa_mask.h: row i sits at key position i + off and
+  // sees keys [pos - wl, pos + wr] (a negative width is unbounded; causal is
+  // folded into wr = 0)
   int off;
   int wl;
   int wr;

@@ -24,6 +24,8 @@ Workloads (sizes as [B, H, N, d]):
                   sequence (its last 4 positions, causal), q from seed 305.
 * ``backward``    the prefill Q, K, V plus an upstream gradient dLoss/dO
                   ~ N(0,1) from seed 203.
+* ``window``      the prefill Q, K, V with a causal sliding window of 1024
+                  keys (each row sees its own position and the 1023 before).
 
 Workload k draws Q/K/V from seed k; bias, k_len and the special rows come
 from a second generator seeded 100 + k.  Small workloads are drawn on the CPU
@@ -46,6 +48,7 @@ SHAPES = {
     "decode": dict(B=64, H=32, Nq=1, Nk=8192, dk=128, dv=128),
     "backward": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
     "decode_mq": dict(B=64, H=32, Nq=4, Nk=8192, dk=128, dv=128),
+    "window": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
 }
 
 DESCRIPTIONS = {
@@ -57,6 +60,7 @@ DESCRIPTIONS = {
     "backward": "attention bwd (dQ, dK, dV by recomputation) 4x32x4096x4096 d128 bf16 causal, upstream gradient N(0,1)",
     "decode_mq": "split-K multi-query decode 64x32 sequences x 4 query rows (causal), KV lengths U[1,8192], d128 bf16, "
                  "512-key chunks",
+    "window": "attention fwd prefill 4x32x4096x4096 d128 bf16 causal, sliding window of 1024 keys",
 }
 
 
@@ -114,6 +118,14 @@ def prefill(device):
     k = _randn_dev(g, (s["B"], s["H"], s["Nk"], s["dk"]), device, torch.bfloat16)
     v = _randn_dev(g, (s["B"], s["H"], s["Nk"], s["dv"]), device, torch.bfloat16)
     return dict(q=q, k=k, v=v, bias=None, k_len=None, causal=True, scale=1.0 / math.sqrt(128), block_n=0)
+
+
+def window(device):
+    """The prefill workload's Q, K, V (same seed, same draws) under a causal
+    sliding window of 1024 keys (left width 1023)."""
+    inp = prefill(device)
+    inp["window_left"] = 1023
+    return inp
 
 
 def backward(device):
