@@ -27,6 +27,9 @@ Modules:
   itself (tile-size and order invariance, the printed chunk states).
 * ``backward`` -- gradients by recomputation from the saved output and
   log-sum-exp ([GS] section 7; [VW] Step 8).
+* ``dropout`` -- the counter-based dropout mask (Philox4x32-10 from its
+  published definition) that forward and backward both replay ([GS]
+  section 6).
 
 Parity pins: every function here is pinned by ``-m "not gpu"`` tests against
 the pages' printed worked examples, closed forms, invariants and an
@@ -34,6 +37,7 @@ independent library routine; no function is "parity unpinned".
 """
 
 from .backward import attention_bwd_head, attention_bwd_ref
+from .dropout import dropout_bytes, keep_mask, keep_scale, philox4x32_10
 from .dense import allowed_mask, attention_head, attention_ref
 from .online import block_state, even_tiles, merge_states, online_ref
 
@@ -44,7 +48,11 @@ __all__ = [
     "attention_head",
     "attention_ref",
     "block_state",
+    "dropout_bytes",
     "even_tiles",
+    "keep_mask",
+    "keep_scale",
     "merge_states",
     "online_ref",
+    "philox4x32_10",
 ]

@@ -19,7 +19,16 @@ scores, and for an upstream gradient G (row g_i = dLoss/do_i):
     dK    = scale * D^T Q
 
 The Q and K gradients carry the original scale ([GS] section 7).  The bias is
-fixed (no gradient).  Readings where the pages stop short:
+fixed (no gradient).  With dropout ([GS] section 6: the backward must replay
+the forward's random mask and scaling) the forward used P~ = (Z o P) * r,
+Z the kept elements and r = 256/keep_256 (``oracle.dropout``), so
+
+    dV    = P~^T G
+    D_ij  = p_ij (z_ij r (g_i . v_j) - c_i),   c_i = g_i . o_i
+
+(c_i = sum_j p_ij z_ij r (g_i . v_j) = g_i . o_i still holds because o_i is
+the dropped output); dQ and dK follow from D as above.  Readings where the
+pages stop short:
 
 * A row with no allowed key (empty J_i) has the convention o_i = 0 and
   lse_i = -inf ([GS] section 6).  [GS] section 7 says not to read that
@@ -39,10 +48,12 @@ Inputs are converted to float64 exactly; ``scale`` is used as given.
 import numpy as np
 
 from .dense import allowed_mask, attention_head
+from .dropout import keep_mask, keep_scale
 
 
 def attention_bwd_head(q, k, v, g, *, scale, nq, causal=False, k_len_b=None,
-                       bias=None, row_ids=None, o=None, lse=None):
+                       bias=None, row_ids=None, o=None, lse=None, align="bottom_right",
+                       window=(None, None), dropout=None, bh=0):
     """Gradients for selected query rows of one (batch, head).
 
     q: [R, dk] rows ``row_ids`` (default 0..R-1) of a query axis of length
@@ -63,13 +74,14 @@ def attention_bwd_head(q, k, v, g, *, scale, nq, causal=False, k_len_b=None,
 
     if o is None or lse is None:
         o_f, lse_f = attention_head(q, k, v, scale=scale, nq=nq, causal=causal,
-                                    k_len_b=k_len_b, bias=bias, row_ids=row_ids)
+                                    k_len_b=k_len_b, bias=bias, row_ids=row_ids, align=align,
+                                    window=window, dropout=dropout, bh=bh)
         o = o_f if o is None else o
         lse = lse_f if lse is None else lse
     o = np.asarray(o, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)
 
-    ok = allowed_mask(row_ids, nq, nk, causal, k_len_b)
+    ok = allowed_mask(row_ids, nq, nk, causal, k_len_b, align=align, window=window)
     nonempty = ok.any(axis=1) & np.isfinite(lse)
     s = (q @ k.T) * float(scale)
     if bias is not None:
@@ -78,19 +90,25 @@ def attention_bwd_head(q, k, v, g, *, scale, nq, causal=False, k_len_b=None,
     p = np.where(ok & nonempty[:, None], np.exp(np.where(ok, s, 0.0) - lse_safe[:, None]), 0.0)
 
     c = np.sum(g * o, axis=1)                      # c_i = g_i . o_i
-    d = p * (g @ v.T - c[:, None])                 # dLoss / ds_ij
-    dv = p.T @ g
+    if dropout is None:
+        zr = 1.0                                   # no dropout: z = 1, r = 1
+    else:
+        keep_256, seed = dropout
+        zr = np.where(keep_mask(bh, row_ids, nk, seed, keep_256), keep_scale(keep_256), 0.0)
+    d = p * (zr * (g @ v.T) - c[:, None])          # dLoss / ds_ij
+    dv = (p * zr).T @ g
     dq = float(scale) * (d @ k)
     dk = float(scale) * (d.T @ q)
     return dq, dk, dv
 
 
 def attention_bwd_ref(q, k, v, g, *, scale, causal=False, k_len=None, bias=None,
-                      o=None, lse=None):
+                      o=None, lse=None, align="bottom_right", window=(None, None), dropout=None):
     """Gradients over a whole batch: q [B,H,Nq,dk], k [B,H,Nk,dk],
     v [B,H,Nk,dv], g [B,H,Nq,dv]; optional k_len [B], bias [B,H,Nq,Nk], and
     the forward's o [B,H,Nq,dv] / lse [B,H,Nq] to use in place of the
-    oracle's own.  Returns (dq, dk, dv) in float64."""
+    oracle's own; ``align``, ``window`` and ``dropout`` as for the forward.
+    Returns (dq, dk, dv) in float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -105,6 +123,7 @@ def attention_bwd_ref(q, k, v, g, *, scale, causal=False, k_len=None, bias=None,
             res = attention_bwd_head(
                 q[b, h], k[b, h], v[b, h], g[b, h], scale=scale, nq=nq, causal=causal,
                 k_len_b=klb, bias=None if bias is None else bias[b, h],
-                o=None if o is None else o[b, h], lse=None if lse is None else lse[b, h])
+                o=None if o is None else o[b, h], lse=None if lse is None else lse[b, h],
+                align=align, window=window, dropout=dropout, bh=b * heads + h)
             dq[b, h], dk[b, h], dv[b, h] = res
     return dq, dk, dv

@@ -43,6 +43,8 @@ the GPU receives.
 
 import numpy as np
 
+from .dropout import keep_mask, keep_scale
+
 _ROW_BLOCK = 2048  # rows of S materialised at once; every row is complete
 
 
@@ -72,13 +74,18 @@ def allowed_mask(row_ids, nq, nk, causal, k_len_b, align="bottom_right", window=
 
 def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
                    bias=None, row_ids=None, return_p=False, align="bottom_right",
-                   window=(None, None)):
+                   window=(None, None), dropout=None, bh=0):
     """Dense attention for selected query rows of one (batch, head).
 
     q: [R, dk] the query rows whose global indices are ``row_ids`` (default
     0..R-1) on a query axis of length ``nq``; k: [Nk, dk]; v: [Nk, dv];
     bias: [R, Nk] or None, added after scaling ([GS] section 1).
-    Returns (o [R, dv], lse [R]) and, if ``return_p``, also P [R, Nk].
+    dropout: None or (keep_256, seed): the probabilities are dropped with the
+    counter-based mask of head ``bh`` = b*H + h and the kept ones scaled by
+    256/keep_256 before the product with V; lse is the undropped one
+    (``oracle.dropout``).
+    Returns (o [R, dv], lse [R]) and, if ``return_p``, also P [R, Nk] (the
+    undropped probabilities).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -101,7 +108,12 @@ def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
     ell = e.sum(axis=1)
     safe_ell = np.where(nonempty, ell, 1.0)
     p = e / safe_ell[:, None]
-    o = p @ v
+    if dropout is None:
+        o = p @ v
+    else:
+        keep_256, seed = dropout
+        z = keep_mask(bh, row_ids, nk, seed, keep_256)
+        o = (np.where(z, p, 0.0) * keep_scale(keep_256)) @ v
     lse = np.where(nonempty, m + np.log(safe_ell), -np.inf)
     o[~nonempty] = 0.0
     p[~nonempty] = 0.0
@@ -111,7 +123,7 @@ def attention_head(q, k, v, *, scale, nq, causal=False, k_len_b=None,
 
 
 def attention_ref(q, k, v, *, scale, causal=False, k_len=None, bias=None,
-                  return_p=False, align="bottom_right", window=(None, None)):
+                  return_p=False, align="bottom_right", window=(None, None), dropout=None):
     """Dense attention over a whole batch: q [B,H,Nq,dk], k [B,H,Nk,dk],
     v [B,H,Nk,dv], k_len [B] or None, bias [B,H,Nq,Nk] or None.
 
@@ -137,7 +149,8 @@ def attention_ref(q, k, v, *, scale, causal=False, k_len=None, bias=None,
                                      scale=scale, nq=nq, causal=causal,
                                      k_len_b=klb, bias=bb,
                                      row_ids=np.arange(r0, r1),
-                                     return_p=return_p, align=align, window=window)
+                                     return_p=return_p, align=align, window=window,
+                                     dropout=dropout, bh=b * heads + h)
                 o[b, h, r0:r1] = res[0]
                 lse[b, h, r0:r1] = res[1]
                 if return_p:

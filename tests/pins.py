@@ -713,6 +713,149 @@ def pin_bwd_single_key(orc):
     _close(dq[0, 0, 0], np.zeros(3), 1e-15, "row 0 under causal sees key 0 only")
 
 
+# --------------------------------------------------------------------------
+# dropout with a counter-based mask ([GS] section 6: the backward replays the
+# forward's mask and scaling)
+# --------------------------------------------------------------------------
+
+def pin_philox_known_answers(orc):
+    """The generator reproduces the published known-answer vectors of
+    Philox4x32-10 (tests/golden/philox4x32_10_kat.json)."""
+    with open(GOLDEN / "philox4x32_10_kat.json") as f:
+        fx = json.load(f)
+    for vec in fx["vectors"]:
+        ctr = np.array([int(x, 16) for x in vec["counter"]], dtype=np.uint32)
+        key = np.array([int(x, 16) for x in vec["key"]], dtype=np.uint32)
+        want = [int(x, 16) for x in vec["output"]]
+        got = [int(x) for x in orc.philox4x32_10(ctr, key)]
+        assert got == want, (vec, [f"{x:08x}" for x in got])
+
+
+def pin_philox_statistics(orc):
+    """Bytes of consecutive counters are uniform (chi-square over 256 bins),
+    and flipping any one counter or key bit flips about half of the 128
+    output bits (avalanche)."""
+    n = 1 << 16
+    ctr = np.zeros((n, 4), dtype=np.uint32)
+    ctr[:, 0] = np.arange(n, dtype=np.uint32)
+    ctr[:, 2] = 7
+    words = orc.philox4x32_10(ctr, np.array([12345, 678], dtype=np.uint32))
+    by = np.frombuffer(words.astype("<u4").tobytes(), dtype=np.uint8)
+    hist = np.bincount(by, minlength=256).astype(np.float64)
+    exp = by.size / 256.0
+    chi2 = float(np.sum((hist - exp) ** 2 / exp))
+    assert 170.0 < chi2 < 350.0, f"byte chi-square {chi2:.1f} over 255 degrees of freedom"
+    rng = np.random.default_rng(5)
+    base_c = rng.integers(0, 1 << 32, (256, 4), dtype=np.uint64).astype(np.uint32)
+    base_k = rng.integers(0, 1 << 32, (256, 2), dtype=np.uint64).astype(np.uint32)
+    out0 = orc.philox4x32_10(base_c, base_k)
+
+    def flipped(a, b):
+        x = (a ^ b).astype(np.uint64)
+        return sum(int(bin(int(w)).count("1")) for w in x.reshape(-1)) / a.shape[0]
+
+    for word in range(4):
+        for bit in (0, 13, 31):
+            c = base_c.copy()
+            c[:, word] ^= np.uint32(1 << bit)
+            mean = flipped(out0, orc.philox4x32_10(c, base_k))
+            assert abs(mean - 64.0) < 3.0, (word, bit, mean)
+    for word in range(2):
+        k = base_k.copy()
+        k[:, word] ^= np.uint32(1 << 17)
+        assert abs(flipped(out0, orc.philox4x32_10(base_c, k)) - 64.0) < 3.0
+
+
+def pin_dropout_mask_layout(orc):
+    """The vectorised mask follows the stated layout element by element
+    (counter (i, j div 64, b*H+h, (j div 4) mod 4), byte j mod 4 of word
+    (j div 16) mod 4), keeps about keep_256/256 of the elements, and
+    keep_256 = 256 keeps everything."""
+    seed, bh, rows, nk = 0x1234_5678_9ABC_DEF0, 5, [0, 3, 70, 129], 200
+    got = orc.dropout_bytes(bh, rows, nk, seed)
+    key = np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint32)
+    for a, i in enumerate(rows):
+        for j in range(nk):
+            ctr = np.array([i, j // 64, bh, (j // 4) % 4], dtype=np.uint32)
+            word = int(orc.philox4x32_10(ctr, key)[(j // 16) % 4])
+            assert int(got[a, j]) == (word >> (8 * (j % 4))) & 0xFF, (i, j)
+    z = orc.keep_mask(3, np.arange(256), 512, 99, 230)
+    rate, n = float(z.mean()), z.size
+    sigma = math.sqrt(230 / 256 * (26 / 256) / n)
+    assert abs(rate - 230 / 256) < 5 * sigma, rate
+    assert orc.keep_mask(0, np.arange(8), 64, 1, 256).all()
+    assert orc.keep_scale(230) == 256.0 / 230.0
+    # different heads, rows and seeds draw different masks
+    assert not np.array_equal(orc.dropout_bytes(0, [0], 64, 1), orc.dropout_bytes(1, [0], 64, 1))
+    assert not np.array_equal(orc.dropout_bytes(0, [0], 64, 1), orc.dropout_bytes(0, [1], 64, 1))
+    assert not np.array_equal(orc.dropout_bytes(0, [0], 64, 1), orc.dropout_bytes(0, [0], 64, 2))
+
+
+def pin_dropout_forward(orc):
+    """Forward with dropout: equals torch float64 attention with the mask
+    applied to softmax(S) and the kept values scaled by 256/T; lse is the
+    undropped one; T = 256 is no dropout, bit for bit; averaged over many
+    seeds the dropped output approaches the undropped one."""
+    import torch
+
+    rng = np.random.default_rng(71)
+    bsz, heads, nq, nk, dk, dv = 2, 2, 5, 70, 4, 3
+    q = rng.standard_normal((bsz, heads, nq, dk))
+    k = rng.standard_normal((bsz, heads, nk, dk))
+    v = rng.standard_normal((bsz, heads, nk, dv))
+    kw = dict(scale=0.6, causal=True, k_len=[70, 40])
+    o0, l0 = orc.attention_ref(q, k, v, **kw)
+    o_t, l_t = orc.attention_ref(q, k, v, dropout=(256, 77), **kw)
+    assert np.array_equal(o0, o_t) and np.array_equal(l0, l_t)
+    t, seed = 200, 0xABCDEF
+    o, lse = orc.attention_ref(q, k, v, dropout=(t, seed), **kw)
+    assert np.array_equal(lse, l0), "dropout must not change lse"
+    for b in range(bsz):
+        lim = kw["k_len"][b]
+        for h in range(heads):
+            s = torch.from_numpy(q[b, h]) @ torch.from_numpy(k[b, h]).T * 0.6
+            i = torch.arange(nq)[:, None]
+            j = torch.arange(nk)[None, :]
+            allowed = (j <= i + nk - nq) & (j < lim)
+            p = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=1)
+            p = torch.nan_to_num(p, nan=0.0)
+            z = torch.from_numpy(orc.keep_mask(b * heads + h, np.arange(nq), nk, seed, t))
+            ref = (p * z * (256.0 / t)) @ torch.from_numpy(v[b, h])
+            _close(o[b, h], ref.numpy(), 1e-12, "dropout forward vs torch")
+    samples = np.stack([orc.attention_ref(q, k, v, dropout=(t, sd), **kw)[0] for sd in range(300)])
+    mean, err = samples.mean(axis=0), samples.std(axis=0) / math.sqrt(300)
+    assert np.all(np.abs(mean - o0) <= 5 * err + 1e-12), float(np.max(np.abs(mean - o0) / (err + 1e-300)))
+
+
+def pin_dropout_backward(orc):
+    """Backward with dropout: torch autograd (float64) of softmax, the fixed
+    dropout mask and its scaling gives the oracle's dQ, dK, dV; the oracle is
+    given its own dropped forward output."""
+    import torch
+
+    rng = np.random.default_rng(73)
+    bsz, heads, nq, nk, dk, dv = 1, 2, 6, 70, 4, 5
+    q, k, v, g = _bwd_case(rng, bsz, heads, nq, nk, dk, dv)
+    t, seed, scale = 180, 31337, 0.45
+    dq, dk_, dv_ = orc.attention_bwd_ref(q, k, v, g, scale=scale, causal=True, dropout=(t, seed))
+    for h in range(heads):
+        tq = torch.from_numpy(q[0, h]).clone().requires_grad_(True)
+        tk = torch.from_numpy(k[0, h]).clone().requires_grad_(True)
+        tv = torch.from_numpy(v[0, h]).clone().requires_grad_(True)
+        i = torch.arange(nq)[:, None]
+        j = torch.arange(nk)[None, :]
+        allowed = j <= i + nk - nq
+        s = (tq @ tk.T) * scale
+        p = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=1)
+        z = torch.from_numpy(orc.keep_mask(h, np.arange(nq), nk, seed, t))
+        o = (p * z * (256.0 / t)) @ tv
+        loss = (o * torch.from_numpy(g[0, h])).sum()
+        gq, gk, gv = torch.autograd.grad(loss, (tq, tk, tv))
+        _close(dq[0, h], gq.numpy(), 1e-12, "dropout dQ vs autograd")
+        _close(dk_[0, h], gk.numpy(), 1e-12, "dropout dK vs autograd")
+        _close(dv_[0, h], gv.numpy(), 1e-12, "dropout dV vs autograd")
+
+
 PINS = [
     pin_gs_sec2_tile_local_counterexample,
     pin_gs_sec4_rescale_both,
@@ -731,6 +874,11 @@ PINS = [
     pin_sampled_rows,
     pin_mask_variants,
     pin_bwd_autograd,
+    pin_philox_known_answers,
+    pin_philox_statistics,
+    pin_dropout_mask_layout,
+    pin_dropout_forward,
+    pin_dropout_backward,
     pin_bwd_finite_differences,
     pin_bwd_invariants,
     pin_bwd_single_key,

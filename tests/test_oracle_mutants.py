@@ -115,9 +115,9 @@ MUTANTS = [
      "ok &= j <= pos + int(wr)", "ok &= j <= pos + nk"),
     # --- backward by recomputation ------------------------------------------
     ("bwd_c_dropped", "backward.py",
-     "d = p * (g @ v.T - c[:, None])", "d = p * (g @ v.T)"),
+     "d = p * (zr * (g @ v.T) - c[:, None])", "d = p * (zr * (g @ v.T))"),
     ("bwd_c_sign", "backward.py",
-     "d = p * (g @ v.T - c[:, None])", "d = p * (g @ v.T + c[:, None])"),
+     "d = p * (zr * (g @ v.T) - c[:, None])", "d = p * (zr * (g @ v.T) + c[:, None])"),
     ("bwd_c_from_v", "backward.py",
      "c = np.sum(g * o, axis=1)", "c = np.sum(g, axis=1) * 0.5"),
     ("bwd_dq_unscaled", "backward.py",
@@ -129,9 +129,9 @@ MUTANTS = [
     ("bwd_dq_uses_v", "backward.py",
      "dq = float(scale) * (d @ k)", "dq = float(scale) * (d @ v[:, :1].repeat(k.shape[1], axis=1))"),
     ("bwd_dv_uses_d", "backward.py",
-     "dv = p.T @ g", "dv = d.T @ g"),
+     "dv = (p * zr).T @ g", "dv = (d * zr).T @ g"),
     ("bwd_dv_rows_reversed", "backward.py",
-     "dv = p.T @ g", "dv = p.T @ g[::-1]"),
+     "dv = (p * zr).T @ g", "dv = (p * zr).T @ g[::-1]"),
     ("bwd_lse_sign", "backward.py",
      "np.exp(np.where(ok, s, 0.0) - lse_safe[:, None])", "np.exp(np.where(ok, s, 0.0) + lse_safe[:, None])"),
     ("bwd_mask_ignored", "backward.py",
@@ -140,6 +140,27 @@ MUTANTS = [
      "s = s + np.asarray(bias, dtype=np.float64)", "s = s"),
     ("bwd_scale_dropped_in_logits", "backward.py",
      "s = (q @ k.T) * float(scale)", "s = (q @ k.T)"),
+    # --- dropout -------------------------------------------------------------
+    ("philox_no_key_bump", "dropout.py", "if rnd < 9:", "if rnd < 0:"),
+    ("philox_nine_rounds", "dropout.py", "for rnd in range(10):", "for rnd in range(9):"),
+    ("philox_multipliers_swapped", "dropout.py",
+     "p0 = c0.astype(np.uint64) * _M0", "p0 = c0.astype(np.uint64) * _M1"),
+    ("philox_output_order", "dropout.py",
+     "c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0", "c0, c1, c2, c3 = hi0 ^ c1 ^ k0, lo1, hi1 ^ c3 ^ k1, lo0"),
+    ("dropout_head_ignored", "dropout.py", "ctr[..., 2] = int(bh)", "ctr[..., 2] = 0"),
+    ("dropout_word_index", "dropout.py", "((j >> 4) & 3)[None, :, None]", "((j >> 2) & 3)[None, :, None]"),
+    ("dropout_byte_shift", "dropout.py", "(8 * (j & 3))", "(8 * ((j >> 4) & 3))"),
+    ("dropout_keep_le", "dropout.py",
+     "return dropout_bytes(bh, row_ids, nk, seed).astype(np.int64) < t",
+     "return dropout_bytes(bh, row_ids, nk, seed).astype(np.int64) <= t"),
+    ("dropout_scale_255", "dropout.py", "return 256.0 / float(keep_256)", "return 255.0 / float(keep_256)"),
+    ("dropout_fwd_unscaled", "dense.py",
+     "o = (np.where(z, p, 0.0) * keep_scale(keep_256)) @ v", "o = np.where(z, p, 0.0) @ v"),
+    ("dropout_fwd_mask_inverted", "dense.py",
+     "o = (np.where(z, p, 0.0) * keep_scale(keep_256)) @ v", "o = (np.where(z, 0.0, p) * keep_scale(keep_256)) @ v"),
+    ("dropout_bwd_ignored_in_d", "backward.py",
+     "d = p * (zr * (g @ v.T) - c[:, None])", "d = p * ((g @ v.T) - c[:, None])"),
+    ("dropout_bwd_ignored_in_dv", "backward.py", "dv = (p * zr).T @ g", "dv = p.T @ g"),
 ]
 
 
