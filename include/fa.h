@@ -37,6 +37,8 @@
  *   both dtypes; bf16 inputs use bf16 MFMA products (P is rounded to bf16
  *   before P.V), fp32 inputs use fp32 MFMA.
  * - The library is stateless and reentrant.
+ * - fa_fwd_ex / fa_bwd_ex add the mask variants of [GS] section 6 (top-left
+ *   alignment, sliding windows) and dropout with a counter-based mask.
  */
 #ifndef ONLINE_SOFTMAX_FA_H
 #define ONLINE_SOFTMAX_FA_H
@@ -117,24 +119,42 @@ typedef enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 } fa_align;
  *             j <= pos_i + window_right if window_right >= 0 }.
  * The usual sliding window of width W is causal = 1, window_left = W - 1.
  * Rows whose J_i is empty (a window entirely past k_len, or before key 0)
- * get o_i = 0, lse_i = -inf.  With align = BOTTOM_RIGHT and both widths -1
- * the result equals fa_fwd's bit for bit.  Every kernel (both dtypes, the
- * bf16 head-dim 64/128 fast path included) visits only the key tiles that
- * meet the union of a row block's ranges and masks only the edge tiles.
- * Returns FA_ERR_UNSUPPORTED for another align value or a width below -1.
+ * get o_i = 0, lse_i = -inf.  Every kernel (both dtypes, the bf16 head-dim
+ * 64/128 fast path included) visits only the key tiles that meet the union
+ * of a row block's ranges and masks only the edge tiles.
+ *
+ *   keep_256     dropout of the attention probabilities ([GS] section 6:
+ *                a training backward must replay the mask and scaling):
+ *                256 = no dropout; T in 1..255 keeps an element iff its
+ *                random byte is < T (keep probability T/256) and multiplies
+ *                kept probabilities by 256/T:
+ *                  o_i = (256/T) sum_j z_ij p_ij v_j,  lse_i undropped.
+ *   seed         64-bit seed of the dropout mask (ignored without dropout).
+ *
+ * Dropout mask layout: the random byte of element (b, h, i, j) comes from
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+ * Easy as 1, 2, 3", SC 2011) with key (seed mod 2^32, seed div 2^32) and
+ * counter (i, j div 64, b*H + h, (j div 4) mod 4); it is byte (j mod 4)
+ * (bits 8(j mod 4) .. +7) of output word (j div 16) mod 4.  fa_bwd_ex with
+ * the same seed and keep_256 replays the same mask.
+ *
+ * With align = BOTTOM_RIGHT, both widths -1 and keep_256 = 256 the result
+ * equals fa_fwd's bit for bit.  Returns FA_ERR_UNSUPPORTED for another align
+ * value, a width below -1 or keep_256 outside 1..256.
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias,
               const int32_t* k_len, void* o, float* lse, int B, int H,
               int Nq, int Nk, int dk, int dv, int dtype, float scale,
               int causal, int align, int window_left, int window_right,
-              int block_n, void* stream);
+              int keep_256, uint64_t seed, int block_n, void* stream);
 
 /* Host-only validation of fa_fwd_ex's arguments. */
 int fa_check_fwd_ex(const void* q, const void* k, const void* v,
                     const float* bias, const int32_t* k_len, const void* o,
                     const float* lse, int B, int H, int Nq, int Nk, int dk,
                     int dv, int dtype, float scale, int causal, int align,
-                    int window_left, int window_right, int block_n);
+                    int window_left, int window_right, int keep_256,
+                    uint64_t seed, int block_n);
 
 /*
  * Bytes of fp32 workspace fa_decode_splitk needs:
@@ -269,6 +289,40 @@ int fa_check_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dv, int B, int H, int Nq, int Nk, int d_k,
                  int d_v, int dtype, float scale, int causal,
                  const void* workspace, size_t workspace_bytes);
+
+/*
+ * fa_bwd_ex -- fa_bwd for the forwards of fa_fwd_ex: the same position
+ * masks (causal, align, window_left, window_right) and the same dropout
+ * (keep_256, seed), replayed exactly ([GS] section 6: the backward must
+ * reproduce the forward's random mask and scaling).  With dropout, for
+ * r = 256/keep_256 and z the kept elements:
+ *
+ *   dV = (z r P)^T dO,   D_ij = p_ij (z_ij r (dO_i . v_j) - c_i),
+ *   c_i = dO_i . O_i (the dropped forward output),
+ *   dQ = scale D K,   dK = scale D^T Q.
+ *
+ * o and lse must be those fa_fwd_ex returned for the same arguments.  Other
+ * arguments, workspace and errors as for fa_bwd; FA_ERR_UNSUPPORTED also for
+ * an invalid align, a width below -1 or keep_256 outside 1..256.  With the
+ * defaults (BOTTOM_RIGHT, -1, -1, 256) it equals fa_bwd bit for bit.
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, const float* bias,
+              const int32_t* k_len, void* dq, void* dk, void* dv, int B,
+              int H, int Nq, int Nk, int d_k, int d_v, int dtype, float scale,
+              int causal, int align, int window_left, int window_right,
+              int keep_256, uint64_t seed, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Host-only validation of fa_bwd_ex's arguments. */
+int fa_check_bwd_ex(const void* q, const void* k, const void* v,
+                    const void* o, const void* dout, const float* lse,
+                    const float* bias, const int32_t* k_len, const void* dq,
+                    const void* dk, const void* dv, int B, int H, int Nq,
+                    int Nk, int d_k, int d_v, int dtype, float scale,
+                    int causal, int align, int window_left, int window_right,
+                    int keep_256, uint64_t seed, const void* workspace,
+                    size_t workspace_bytes);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(int status);

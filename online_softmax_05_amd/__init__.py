@@ -25,7 +25,7 @@ __all__ = [
     "FA_F32", "FA_BF16", "FaError", "lib", "lib_path",
     "FA_ALIGN_BOTTOM_RIGHT", "FA_ALIGN_TOP_LEFT",
     "fa_fwd", "fa_fwd_ex", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
-    "fa_check_fwd", "fa_check_fwd_ex", "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
+    "fa_check_fwd", "fa_check_fwd_ex", "fa_check_decode", "fa_bwd_ex", "fa_check_bwd_ex", "keep_256_for", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
     "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes", "fa_check_decode_mq",
     "fa_status_str", "fa_abi_version",
 ]
@@ -42,15 +42,19 @@ _LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 _lib = None
 
 _vp, _fp, _ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
-_i, _f, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_i, _f, _sz, _u64 = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
 
 _SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_check_fwd": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i]),
     "fa_fwd_ex": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i,
-                       _vp]),
+                       _u64, _i, _vp]),
     "fa_check_fwd_ex": (_i, [_vp, _vp, _vp, _fp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i,
-                             _i]),
+                             _i, _u64, _i]),
+    "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _ip, _vp, _vp, _vp,
+                       _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i, _u64, _vp, _sz, _vp]),
+    "fa_check_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _fp, _fp, _ip, _vp, _vp, _vp,
+                             _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i, _u64, _vp, _sz]),
     "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
@@ -125,10 +129,20 @@ def fa_check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scal
 
 
 def fa_check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align,
-                    window_left, window_right, block_n):
+                    window_left, window_right, keep_256, seed, block_n):
     """Host-only validation of fa_fwd_ex; pointers are plain integers (or None)."""
     return lib().fa_check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale,
-                                 int(causal), int(align), int(window_left), int(window_right), block_n)
+                                 int(causal), int(align), int(window_left), int(window_right), int(keep_256),
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, block_n)
+
+
+def keep_256_for(dropout_p):
+    """The byte threshold T of a dropout probability p: round((1 - p) * 256),
+    at least 1 (keep probability T/256; T = 256 is no dropout)."""
+    p = float(dropout_p)
+    if not 0.0 <= p < 1.0:
+        raise FaError(3, f"dropout probability must lie in [0, 1), got {p}")
+    return max(1, min(256, int(round((1.0 - p) * 256.0))))
 
 
 def fa_check_decode(q, k, v, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, workspace,
@@ -218,21 +232,31 @@ def fa_fwd(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, block_n=
     return out, lse
 
 
-def fa_fwd_ex(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, align="bottom_right",
-              window_left=None, window_right=None, block_n=0, out=None, lse=None, want_lse=True):
-    """fa_fwd with the mask variants: ``align`` "bottom_right" (row i at key
-    position i + Nk - Nq) or "top_left" (at position i); ``window_left`` /
-    ``window_right`` None (open) or a width w >= 0 around that position."""
+def _masks(align, window_left, window_right, keep_256, dropout_p):
     if align not in _ALIGN:
         raise FaError(3, f"align must be one of {sorted(_ALIGN)}, got {align!r}")
     wl = -1 if window_left is None else int(window_left)
     wr = -1 if window_right is None else int(window_right)
     if wl < 0 and window_left is not None or wr < 0 and window_right is not None:
         raise FaError(3, "window widths must be None or >= 0")
+    keep = keep_256_for(dropout_p) if keep_256 is None else int(keep_256)
+    return _ALIGN[align], wl, wr, keep
+
+
+def fa_fwd_ex(q, k, v, *, bias=None, k_len=None, scale=None, causal=False, align="bottom_right",
+              window_left=None, window_right=None, dropout_p=0.0, keep_256=None, seed=0, block_n=0, out=None,
+              lse=None, want_lse=True):
+    """fa_fwd with the mask variants and dropout: ``align`` "bottom_right"
+    (row i at key position i + Nk - Nq) or "top_left" (at position i);
+    ``window_left`` / ``window_right`` None (open) or a width w >= 0 around
+    that position; dropout of P with probability ``dropout_p`` (passed as the
+    byte threshold keep_256_for(p), or ``keep_256`` directly) and the 64-bit
+    ``seed`` of the counter-based mask."""
+    al, wl, wr, keep = _masks(align, window_left, window_right, keep_256, dropout_p)
     dims, scale, out, lse = _fwd_prepare(q, k, v, bias, k_len, scale, out, lse, want_lse)
     st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(k_len), _ptr(out), _ptr(lse),
-                         *dims, _dtype_code(q), scale, int(bool(causal)), _ALIGN[align], wl, wr, int(block_n),
-                         _stream(q.device))
+                         *dims, _dtype_code(q), scale, int(bool(causal)), al, wl, wr, keep,
+                         int(seed) & 0xFFFFFFFFFFFFFFFF, int(block_n), _stream(q.device))
     if st != 0:
         raise FaError(st)
     return out, lse
@@ -277,6 +301,14 @@ def fa_bwd_workspace_bytes(B, H, Nq):
     return lib().fa_bwd_workspace_bytes(B, H, Nq)
 
 
+def fa_check_bwd_ex(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale,
+                    causal, align, window_left, window_right, keep_256, seed, workspace, workspace_bytes):
+    """Host-only validation of fa_bwd_ex (integer addresses; nothing is dereferenced)."""
+    return lib().fa_check_bwd_ex(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype,
+                                 float(scale), causal, align, window_left, window_right, keep_256,
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, workspace, workspace_bytes)
+
+
 def fa_check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale,
                  causal, workspace, workspace_bytes):
     """Host-only validation (integer addresses; nothing is dereferenced)."""
@@ -284,12 +316,7 @@ def fa_check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d
                               float(scale), causal, workspace, workspace_bytes)
 
 
-def fa_bwd(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=False, dq=None, dk=None,
-           dv=None, workspace=None):
-    """Gradients of fa_fwd by recomputation from its output ``o`` and ``lse``:
-    q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv], o and dout [B,H,Nq,dv],
-    lse fp32 [B,H,Nq]; bias, k_len, scale and causal as given to fa_fwd.
-    Returns (dq, dk, dv) in the input dtype."""
+def _bwd_prepare(q, k, v, o, dout, lse, bias, k_len, scale, dq, dk, dv, workspace):
     _need(q, "q", dims=4)
     dev = q.device
     _need(k, "k", dtype=q.dtype, dims=4, device=dev)
@@ -318,18 +345,42 @@ def fa_bwd(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=F
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
     else:
         _need(workspace, "workspace", dtype=torch.float32, dims=1, device=dev)
-    if dq is None:
-        dq = torch.empty_like(q)
-    if dk is None:
-        dk = torch.empty_like(k)
-    if dv is None:
-        dv = torch.empty_like(v)
-    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(bias), _ptr(k_len),
-                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d_k, d_v, _dtype_code(q), float(scale),
-                      int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(dev))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ptrs = [_ptr(x) for x in (q, k, v, o, dout, lse, bias, k_len, dq, dk, dv)]
+    return ptrs, (B, H, Nq, Nk, d_k, d_v), float(scale), (dq, dk, dv), workspace
+
+
+def fa_bwd(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=False, dq=None, dk=None,
+           dv=None, workspace=None):
+    """Gradients of fa_fwd by recomputation from its output ``o`` and ``lse``:
+    q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv], o and dout [B,H,Nq,dv],
+    lse fp32 [B,H,Nq]; bias, k_len, scale and causal as given to fa_fwd.
+    Returns (dq, dk, dv) in the input dtype."""
+    ptrs, dims, scale, grads, workspace = _bwd_prepare(q, k, v, o, dout, lse, bias, k_len, scale, dq, dk, dv,
+                                                       workspace)
+    st = lib().fa_bwd(*ptrs, *dims, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+                      workspace.numel() * 4, _stream(q.device))
     if st != 0:
         raise FaError(st)
-    return dq, dk, dv
+    return grads
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, *, bias=None, k_len=None, scale=None, causal=False, align="bottom_right",
+              window_left=None, window_right=None, dropout_p=0.0, keep_256=None, seed=0, dq=None, dk=None, dv=None,
+              workspace=None):
+    """Gradients of fa_fwd_ex: the same masks, alignment, dropout
+    probability (or keep_256) and seed as the forward call that produced
+    ``o`` and ``lse``.  Returns (dq, dk, dv) in the input dtype."""
+    al, wl, wr, keep = _masks(align, window_left, window_right, keep_256, dropout_p)
+    ptrs, dims, scale, grads, workspace = _bwd_prepare(q, k, v, o, dout, lse, bias, k_len, scale, dq, dk, dv,
+                                                       workspace)
+    st = lib().fa_bwd_ex(*ptrs, *dims, _dtype_code(q), scale, int(bool(causal)), al, wl, wr, keep,
+                         int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(workspace), workspace.numel() * 4, _stream(q.device))
+    if st != 0:
+        raise FaError(st)
+    return grads
 
 
 def fa_decode_splitk_mq_workspace_bytes(B, H, Nq, Nk_max, dv, chunk=512):

@@ -54,23 +54,38 @@ int check_fwd(const void* q, const void* k, const void* v, const float* bias, co
   return FA_OK;
 }
 
-int check_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
-                 const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
-                 float scale, int causal, int align, int window_left, int window_right, int block_n) {
+int check_masks(int align, int window_left, int window_right, int keep_256) {
   if (align != FA_ALIGN_BOTTOM_RIGHT && align != FA_ALIGN_TOP_LEFT) return FA_ERR_UNSUPPORTED;
   if (window_left < -1 || window_right < -1) return FA_ERR_UNSUPPORTED;
+  if (keep_256 < 1 || keep_256 > 256) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
+                 const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
+                 float scale, int causal, int align, int window_left, int window_right, int keep_256,
+                 int block_n) {
+  const int st = check_masks(align, window_left, window_right, keep_256);
+  if (st != FA_OK) return st;
   return check_fwd(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, block_n);
 }
 
-// Forward arguments with the position masks folded into (off, wl, wr):
-// causal is the right width 0, which is also the narrowest right window.
+// The position masks folded into (off, wl, wr): causal is the right width 0,
+// which is also the narrowest right window.
+struct Masks {
+  int off, wl, wr;
+};
+Masks fold_masks(int Nq, int Nk, int causal, int align, int window_left, int window_right) {
+  return Masks{align == FA_ALIGN_BOTTOM_RIGHT ? Nk - Nq : 0, window_left, causal ? 0 : window_right};
+}
+
 fa::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
                           void* o, float* lse, int B, int H, int Nq, int Nk, int dk, int dv, float scale,
-                          int causal, int align, int window_left, int window_right, int block_n) {
-  const int off = align == FA_ALIGN_BOTTOM_RIGHT ? Nk - Nq : 0;
-  const int wr = causal ? 0 : window_right;
+                          int causal, int align, int window_left, int window_right, int keep_256, uint64_t seed,
+                          int block_n) {
+  const Masks m = fold_masks(Nq, Nk, causal, align, window_left, window_right);
   fa::FwdArgs a{q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, block_n == 0 ? 64 : block_n,
-                off, window_left, wr};
+                m.off, m.wl, m.wr, keep_256, (uint32_t)seed, (uint32_t)(seed >> 32)};
   return a;
 }
 
@@ -81,6 +96,19 @@ int launch_fwd(const fa::FwdArgs& a, int dtype, void* stream) {
     e = fa::fwd_bf16_fast_eligible(a) ? fa::launch_fwd_bf16_fast(a, s) : fa::launch_fwd_bf16(a, s);
   else
     e = fa::launch_fwd_f32(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               const float* bias, const int32_t* k_len, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+               int d_k, int d_v, int dtype, float scale, int causal, int align, int window_left, int window_right,
+               int keep_256, uint64_t seed, void* workspace, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Masks m = fold_masks(Nq, Nk, causal, align, window_left, window_right);
+  fa::BwdArgs a{q,     k,     v,    o,    dout,     lse,      bias,          k_len, dq, dk, dv,
+                static_cast<float*>(workspace), B, H, Nq, Nk, d_k, d_v, scale, causal,
+                m.off, m.wl,  m.wr, keep_256, (uint32_t)seed, (uint32_t)(seed >> 32)};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -164,14 +192,15 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 extern "C" {
 
-int fa_abi_version(void) { return 103; }
+int fa_abi_version(void) { return 104; }
 
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large shape";
-    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block_n, chunk, causal flag, alignment, window or scale";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported dtype, head dim, block_n, chunk, causal flag, alignment, window, dropout keep or scale";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
@@ -191,26 +220,29 @@ int fa_fwd(const void* q, const void* k, const void* v, const float* bias, const
   if (st != FA_OK) return st;
   if ((long long)B * H * Nq == 0) return FA_OK;
   return launch_fwd(make_fwd_args(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal,
-                                  FA_ALIGN_BOTTOM_RIGHT, -1, -1, block_n),
+                                  FA_ALIGN_BOTTOM_RIGHT, -1, -1, 256, 0, block_n),
                     dtype, stream);
 }
 
 int fa_check_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len,
                     const void* o, const float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype,
-                    float scale, int causal, int align, int window_left, int window_right, int block_n) {
+                    float scale, int causal, int align, int window_left, int window_right, int keep_256,
+                    uint64_t seed, int block_n) {
+  (void)seed;
   return check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align, window_left,
-                      window_right, block_n);
+                      window_right, keep_256, block_n);
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, const float* bias, const int32_t* k_len, void* o,
               float* lse, int B, int H, int Nq, int Nk, int dk, int dv, int dtype, float scale, int causal,
-              int align, int window_left, int window_right, int block_n, void* stream) {
+              int align, int window_left, int window_right, int keep_256, uint64_t seed, int block_n,
+              void* stream) {
   const int st = check_fwd_ex(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, dtype, scale, causal, align,
-                              window_left, window_right, block_n);
+                              window_left, window_right, keep_256, block_n);
   if (st != FA_OK) return st;
   if ((long long)B * H * Nq == 0) return FA_OK;
   return launch_fwd(make_fwd_args(q, k, v, bias, k_len, o, lse, B, H, Nq, Nk, dk, dv, scale, causal, align,
-                                  window_left, window_right, block_n),
+                                  window_left, window_right, keep_256, seed, block_n),
                     dtype, stream);
 }
 
@@ -294,11 +326,33 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                            causal, workspace, workspace_bytes);
   if (st != FA_OK) return st;
   if ((long long)B * H * Nq == 0 && (long long)B * H * Nk == 0) return FA_OK;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  fa::BwdArgs a{q,  k,  v,  o,  dout, lse, bias, k_len, dq,  dk,  dv,
-                static_cast<float*>(workspace), B, H, Nq, Nk, d_k, d_v, scale, causal};
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launch_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale, causal,
+                    FA_ALIGN_BOTTOM_RIGHT, -1, -1, 256, 0, workspace, stream);
+}
+
+int fa_check_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    const float* bias, const int32_t* k_len, const void* dq, const void* dk, const void* dv, int B,
+                    int H, int Nq, int Nk, int d_k, int d_v, int dtype, float scale, int causal, int align,
+                    int window_left, int window_right, int keep_256, uint64_t seed, const void* workspace,
+                    size_t workspace_bytes) {
+  (void)seed;
+  const int st = check_masks(align, window_left, window_right, keep_256);
+  if (st != FA_OK) return st;
+  return check_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale, causal,
+                   workspace, workspace_bytes);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              const float* bias, const int32_t* k_len, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+              int d_k, int d_v, int dtype, float scale, int causal, int align, int window_left, int window_right,
+              int keep_256, uint64_t seed, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = fa_check_bwd_ex(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype,
+                                 scale, causal, align, window_left, window_right, keep_256, seed, workspace,
+                                 workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0 && (long long)B * H * Nk == 0) return FA_OK;
+  return launch_bwd(q, k, v, o, dout, lse, bias, k_len, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, dtype, scale, causal,
+                    align, window_left, window_right, keep_256, seed, workspace, stream);
 }
 
 }  // extern "C"

@@ -17,7 +17,12 @@
 //   dV = P^T G,   dQ = scale D K,   dK = scale D^T Q
 //
 // Rows with lse = -inf (no allowed key) contribute nothing.  The bias is a
-// fixed input (no gradient).  Three launches, all deterministic (no
+// fixed input (no gradient).  The position masks (causal in either
+// alignment, sliding windows) are those of the forward (fa_mask.h).  With
+// dropout ([GS] section 6: the backward replays the forward's mask and
+// scaling) the forward used P~ = z r P (r = 256/keep, fa_dropout.h), so
+// dV = P~^T G and D_ij = p_ij (z_ij r (g_i . v_j) - c_i), c_i = g_i . o_i
+// with the dropped output.  Three launches, all deterministic (no
 // atomics): c per row; dK and dV per key tile looping over query rows; dQ
 // per query tile looping over key tiles.
 //
@@ -25,6 +30,8 @@
 // bf16 inputs, any head dims 1..128, LDS-staged tiles.  bf16 inputs with head
 // dims 64/128 take the matrix-core kernels of fa_bwd_bf16.hip.
 #include "fa_common.h"
+#include "fa_dropout.h"
+#include "fa_mask.h"
 #include "launch.h"
 
 namespace fa {
@@ -102,9 +109,13 @@ __device__ __forceinline__ void load_rows(float* dst, int ld, const T* src, int 
 // from the forward's logit and the saved lse.  Each thread takes two
 // (row, key) entries.
 struct Geom {
-  int nq, nk, klen, shift, causal;
+  int nq, nk, klen;
+  KeyRange mr;  // position masks (fa_mask.h)
   float scale;
   const float* bias_bh;  // [Nq, Nk] of this (b, h) or null
+  DropoutSpec dsp;       // dropout (fa_dropout.h); keep == 256: none
+  float drop_scale;      // 256 / keep
+  uint32_t bh;
 };
 
 __device__ __forceinline__ void pd_block(const GenTiles& t, const Geom& g, int r0, int j0, int dk, int dv) {
@@ -116,15 +127,18 @@ __device__ __forceinline__ void pd_block(const GenTiles& t, const Geom& g, int r
     for (int e = 0; e < dk; ++e) s = fmaf(t.qs[rr * (dk + 1) + e], t.ks[key * (dk + 1) + e], s);
     for (int e = 0; e < dv; ++e) dp = fmaf(t.gs[rr * (dv + 1) + e], t.vs[key * (dv + 1) + e], dp);
     const float l = t.ls[rr];
-    const bool ok = row < g.nq && j < g.klen && (!g.causal || j <= row + g.shift) && l != kNegInf;
+    const bool ok = row < g.nq && j >= key_lo(g.mr, row) && j < key_end(g.mr, row, g.klen) && l != kNegInf;
     float p = 0.f;
     if (ok) {
       float x = s * g.scale;
       if (g.bias_bh != nullptr) x += g.bias_bh[(size_t)row * g.nk + j];
       p = fast_exp2((x - l) * kLog2e);  // exp(s_ij - L_i)
     }
-    t.ps[rr * (kKeys + 1) + key] = p;
-    t.ds[rr * (kKeys + 1) + key] = p * (dp - t.cs[rr]);  // D_ij
+    // dropout: the forward used z r p in place of p (r = 256/keep), so
+    // dV takes z r p and D_ij = p (z r dP_ij - c_i)
+    const float zr = (g.dsp.keep < 256 && !dropout_keep_at(g.dsp, row, j, g.bh)) ? 0.f : g.drop_scale;
+    t.ps[rr * (kKeys + 1) + key] = zr * p;
+    t.ds[rr * (kKeys + 1) + key] = p * (zr * dp - t.cs[rr]);  // D_ij
   }
 }
 
@@ -134,14 +148,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_general_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ c, const float* __restrict__ bias,
     const int32_t* __restrict__ k_len, T* __restrict__ dk, T* __restrict__ dv, int H, int Nq, int Nk, int DK, int DV,
-    float scale, int causal) {
+    float scale, KeyRange mr, DropoutSpec dsp, float drop_scale) {
   extern __shared__ float sm[];
   GenTiles t(sm, DK, DV);
   const size_t bh = blockIdx.y;
   const int b = (int)(bh / H);
   const int j0 = blockIdx.x * kKeys;
-  Geom g{Nq, Nk, clamp_klen(k_len, b, Nk), Nk - Nq, causal, scale,
-         bias == nullptr ? nullptr : bias + bh * Nq * (size_t)Nk};
+  Geom g{Nq, Nk, clamp_klen(k_len, b, Nk), mr, scale, bias == nullptr ? nullptr : bias + bh * Nq * (size_t)Nk,
+         dsp, drop_scale, (uint32_t)bh};
 
   load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, Nk, DK);
   load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, Nk, DV);
@@ -152,9 +166,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_general_kernel(
 #pragma unroll
   for (int m = 0; m < 16; ++m) acc_v[m] = acc_k[m] = 0.f;
 
-  // rows that can see a key of this tile ([GS] section 6: global positions)
-  const int r_lo = causal ? max(0, j0 - g.shift) : 0;
-  const int r_hi = j0 < g.klen ? Nq : 0;
+  // rows that can see a key of this tile below klen ([GS] section 6: global
+  // positions): key_end(r) > j0 and key_lo(r) <= the tile's last such key
+  const int jl = min(j0 + kKeys, g.klen) - 1;
+  const int r_lo = mr.wr >= 0 ? (int)max(0LL, (long long)j0 - mr.off - mr.wr) : 0;
+  const int r_hi = j0 >= g.klen ? 0 : (mr.wl >= 0 ? (int)min((long long)Nq, (long long)jl - mr.off + mr.wl + 1) : Nq);
   for (int r0 = r_lo; r0 < r_hi; r0 += kRows) {
     __syncthreads();  // previous tile's readers are done
     load_rows(t.qs, DK + 1, q + bh * Nq * DK, r0, kRows, Nq, DK);
@@ -194,14 +210,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_general_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ c, const float* __restrict__ bias,
     const int32_t* __restrict__ k_len, T* __restrict__ dq, int H, int Nq, int Nk, int DK, int DV, float scale,
-    int causal) {
+    KeyRange mr, DropoutSpec dsp, float drop_scale) {
   extern __shared__ float sm[];
   GenTiles t(sm, DK, DV);
   const size_t bh = blockIdx.y;
   const int b = (int)(bh / H);
   const int r0 = blockIdx.x * kRows;
-  Geom g{Nq, Nk, clamp_klen(k_len, b, Nk), Nk - Nq, causal, scale,
-         bias == nullptr ? nullptr : bias + bh * Nq * (size_t)Nk};
+  Geom g{Nq, Nk, clamp_klen(k_len, b, Nk), mr, scale, bias == nullptr ? nullptr : bias + bh * Nq * (size_t)Nk,
+         dsp, drop_scale, (uint32_t)bh};
 
   load_rows(t.qs, DK + 1, q + bh * Nq * DK, r0, kRows, Nq, DK);
   load_rows(t.gs, DV + 1, dout + bh * Nq * DV, r0, kRows, Nq, DV);
@@ -216,8 +232,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_general_kernel(
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = 0.f;
 
-  const int kend = visible_key_end(g.klen, causal != 0, min(r0 + kRows, Nq) - 1, Nq, Nk);
-  for (int j0 = 0; j0 < kend; j0 += kKeys) {
+  // key tiles that meet the union of the rows' ranges
+  const int kbeg = key_lo(mr, r0);
+  const int kend = key_end(mr, min(r0 + kRows, Nq) - 1, g.klen);
+  for (int j0 = (kbeg / kKeys) * kKeys; j0 < kend; j0 += kKeys) {
     __syncthreads();
     load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, Nk, DK);
     load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, Nk, DV);
@@ -260,11 +278,14 @@ hipError_t launch_general(const BwdArgs& a, hipStream_t stream) {
   if (a.Nk > 0)  // with no query rows this writes dK = dV = 0
     hipLaunchKernelGGL(bwd_dkdv_general_kernel<T>, dim3((unsigned)((a.Nk + kKeys - 1) / kKeys), bh), dim3(kThreads),
                        smem, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse, a.ws_c,
-                       a.bias, a.k_len, (T*)a.dk_out, (T*)a.dv_out, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale, a.causal);
+                       a.bias, a.k_len, (T*)a.dk_out, (T*)a.dv_out, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale,
+                       KeyRange{a.off, a.wl, a.wr}, DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256},
+                       256.f / (float)a.keep_256);
   if (rows > 0)
     hipLaunchKernelGGL(bwd_dq_general_kernel<T>, dim3((unsigned)((a.Nq + kRows - 1) / kRows), bh), dim3(kThreads),
                        smem, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse, a.ws_c,
-                     a.bias, a.k_len, (T*)a.dq_out, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale, a.causal);
+                     a.bias, a.k_len, (T*)a.dq_out, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale, KeyRange{a.off, a.wl, a.wr},
+                     DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256}, 256.f / (float)a.keep_256);
   return hipGetLastError();
 }
 

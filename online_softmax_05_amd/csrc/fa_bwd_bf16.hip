@@ -31,7 +31,19 @@
 //   dV^T += G^T P,  dK^T += Q^T D   (G^T, Q^T read transposed from LDS)
 // P and D are rounded to bf16 only as matrix-core operands; every sum is
 // fp32.
+//
+// Position masks are the forward's visible key range [lo, end) per row
+// (fa_mask.h); both kernels visit only tiles that meet some row's range and
+// test elements only on edge tiles.  Dropout (a separate instance; [GS]
+// section 6: the backward replays the forward's mask and scaling): with
+// r = 256/keep and z the counter-based mask of fa_dropout.h, dV takes z r P
+// and D = P o (z r dP - c).  In the dQ kernel a lane's 16 keys of a tile are
+// one generator call; in the dK/dV kernel a lane holds one key of 16 rows,
+// so each thread generates one call per query tile (row tid / 4, group
+// tid % 4) into LDS, a tile ahead, and lanes read back the bytes they need.
 #include "fa_common.h"
+#include "fa_dropout.h"
+#include "fa_mask.h"
 #include "fa_tiles.h"
 #include "launch.h"
 
@@ -80,13 +92,13 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
 // dQ
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ cvec,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dq, int H, int Nq,
-    int Nk, float scale, int causal) {
+    int Nk, float scale, KeyRange mr, DropoutSpec dsp, float drop_scale) {
   // one array, buffers addressed by offset (a runtime-indexed table of
   // separate __shared__ arrays would go through a global constant table)
   __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
@@ -100,7 +112,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int b = (int)(bh / H);
   const int q0 = blockIdx.x * kTile;
   const int klen = clamp_klen(k_len, b, Nk);
-  const int shift = Nk - Nq;
   const int row = q0 + 16 * wave + r16;  // this lane's query row
   const bool rvalid = row < Nq;
 
@@ -132,29 +143,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     if (rvalid && g == 0) cvec[bh * Nq + row] = c_row;
   }
   const float c2 = scale * kLog2e;
-  const int row_end = !live ? 0 : (causal ? min(klen, row + shift + 1) : klen);
+  // this row's visible keys [row_lo, row_lo + row_span) (none for a dead row)
+  const int row_lo = key_lo(mr, row);
+  const int row_end = live ? key_end(mr, row, klen) : 0;
+  const unsigned row_span = row_end > row_lo ? (unsigned)(row_end - row_lo) : 0u;
   const float* brow = BIAS ? bias + (bh * Nq + (size_t)(rvalid ? row : 0)) * Nk : nullptr;
 
   f32x4 acc[DK / 16];
 #pragma unroll
   for (int d = 0; d < DK / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kend = visible_key_end(klen, causal != 0, min(q0 + kTile, Nq) - 1, Nq, Nk);
-  const int n_tiles = kend > 0 ? (kend + kTile - 1) / kTile : 0;
-  // tiles visible in full to the work-group's first row need no mask
-  const int first_end = causal ? min(klen, q0 + shift + 1) : klen;
-  const int n_full = min(n_tiles, max(first_end, 0) / kTile);
+  // key tiles that meet the union of the rows' ranges; tiles in
+  // [t_full, t_full_end) lie inside every row's range and need no mask
+  const int last_row = min(q0 + kTile, Nq) - 1;
+  const int kbeg = key_lo(mr, q0);
+  const int kend = key_end(mr, last_row, klen);
+  const int t_begin = kbeg / kTile;
+  const int t_end = kend > kbeg ? (kend + kTile - 1) / kTile : t_begin;
+  const int t_full = (key_lo(mr, last_row) + kTile - 1) / kTile;
+  const int t_full_end = key_end(mr, q0, klen) / kTile;
 
-  if (n_tiles > 0) {
-    load_tile<DK>(kbh, Nk, ka, kbase, wave);
-    load_tile<DV>(vbh, Nk, va, vbase, wave);
+  if (t_begin < t_end) {
+    load_tile<DK>(kbh + (size_t)t_begin * kTile * DK, Nk - t_begin * kTile, ka, kbase, wave);
+    load_tile<DV>(vbh + (size_t)t_begin * kTile * DV, Nk - t_begin * kTile, va, vbase, wave);
   }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int par = t & 1;
+  for (int t = t_begin; t < t_end; ++t) {
+    const int par = (t - t_begin) & 1;
     wait_loads();
     __syncthreads();  // tile t visible; tile t-1's buffers free
     const int j0 = t * kTile;
-    if (t + 1 < n_tiles) {
+    if (t + 1 < t_end) {
       load_tile<DK>(kbh + (size_t)(j0 + kTile) * DK, Nk - (j0 + kTile), ka, kbase + (par ^ 1) * Tile<DK>::BYTES,
                     wave);
       load_tile<DV>(vbh + (size_t)(j0 + kTile) * DV, Nk - (j0 + kTile), va, vbase + (par ^ 1) * Tile<DV>::BYTES,
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     }
     const lds_char* kt = kbase + par * Tile<DK>::BYTES;
     const lds_char* vt = vbase + par * Tile<DV>::BYTES;
-    const bool masked = t >= n_full || !live || BIAS;
+    const bool masked = t < t_full || t >= t_full_end || !live || BIAS;
     // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of `row`
     f32x4 s[4], dp[4];
 #pragma unroll
@@ -173,7 +191,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < DV / 32; ++i) dp[kb] = mfma(frag_read(vt + va.frag[i] + 16 * kb * Tile<DV>::ROW), gf[i], dp[kb]);
     }
-    // P^T and D^T = P^T o (dP^T - c)
+    // P^T and D^T = P^T o (dP^T - c)   (dropout: P^T o (z r dP^T - c))
+    Philox4 zw;
+    if (DROP) zw = dropout_words(dsp, row, t, (uint32_t)bh, g);
     f32x4 dsv[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -185,8 +205,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
         float arg = fmaf(s[kb][j], c2, -l2);
         if (BIAS) arg = fmaf(bv[j], kLog2e, arg);
         float p = fast_exp2(arg);
-        if (masked && key0 + j >= row_end) p = 0.f;
-        dsv[kb][j] = p * (dp[kb][j] - c_row);
+        if (masked && (unsigned)(key0 + j - row_lo) >= row_span) p = 0.f;
+        const float dpz = DROP ? (dropout_keep(zw.x[kb], j, dsp.keep) ? drop_scale * dp[kb][j] : 0.f) : dp[kb][j];
+        dsv[kb][j] = p * (dpz - c_row);
       }
     }
     // dQ^T += K^T D^T over the tile's two 32-key steps
@@ -215,16 +236,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
 // dK and dV
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ cvec,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int H, int Nq, int Nk, float scale, int causal) {
+    uint16_t* __restrict__ dv, int H, int Nq, int Nk, float scale, KeyRange mr, DropoutSpec dsp,
+    float drop_scale) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
-  __shared__ float lbuf[2][kTile];  // L_i log2 e (0 for rows without a key)
-  __shared__ float cbuf[2][kTile];  // c_i
-  __shared__ int ebuf[2][kTile];    // per row: keys < end are allowed
+  __shared__ float lbuf[2][kTile];      // L_i log2 e (0 for rows without a key)
+  __shared__ float cbuf[2][kTile];      // c_i
+  __shared__ int lobuf[2][kTile];       // per row: first visible key
+  __shared__ unsigned spbuf[2][kTile];  // per row: number of visible keys (0 for rows without a key)
+  // dropout words of the query tile: row rr, group g', word w at
+  // [rr * kZRow + 4 g' + w] (kZRow = 17: odd stride, few bank conflicts)
+  constexpr int kZRow = 17;
+  __shared__ uint32_t zbuf[DROP ? 2 : 1][DROP ? kTile * kZRow : 1];
   lds_char* const qbase = (lds_char*)smem;
   lds_char* const gbase = qbase + 2 * Tile<DK>::BYTES;
 
@@ -236,7 +263,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   const int b = (int)(bh / H);
   const int j0 = blockIdx.x * kTile;
   const int klen = clamp_klen(k_len, b, Nk);
-  const int shift = Nk - Nq;
   const int key = j0 + 16 * wave + r16;  // this lane's key
   const bool kvalid = key < Nk;
 
@@ -258,12 +284,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
 #pragma unroll
   for (int d = 0; d < DK / 16; ++d) acc_k[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // query tiles whose rows can see a key of this work-group
-  const int r_lo = causal ? max(0, j0 - shift) : 0;
-  const int t0 = r_lo / kTile;
-  const int t_end = j0 < klen ? (Nq + kTile - 1) / kTile : t0;
-  const int n_tiles = max(t_end - t0, 0);
+  // query tiles whose rows can see a key of this work-group below klen:
+  // key_end(r) > j0 and key_lo(r) <= key_last
   const int key_last = min(j0 + kTile, klen) - 1;
+  const int r_lo = mr.wr >= 0 ? (int)max(0LL, (long long)j0 - mr.off - mr.wr) : 0;
+  const int r_hi = j0 >= klen ? 0 : (mr.wl >= 0 ? (int)min((long long)Nq, (long long)key_last - mr.off + mr.wl + 1) : Nq);
+  const int t0 = r_lo / kTile;
+  const int t_end = r_hi > r_lo ? (r_hi + kTile - 1) / kTile : t0;
+  const int n_tiles = max(t_end - t0, 0);
 
   auto stage_rows = [&](int qt, int buf) {
     if (tid < kTile) {
@@ -273,7 +301,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
       const bool live = l != kNegInf;
       lbuf[buf][tid] = live ? l * kLog2e : 0.f;
       cbuf[buf][tid] = ok ? cvec[bh * Nq + r] : 0.f;
-      ebuf[buf][tid] = !live ? 0 : (causal ? min(klen, r + shift + 1) : klen);
+      const int lo = key_lo(mr, r), end = live ? key_end(mr, r, klen) : 0;
+      lobuf[buf][tid] = lo;
+      spbuf[buf][tid] = end > lo ? (unsigned)(end - lo) : 0u;
+    }
+    if (DROP) {
+      // one generator call per thread: row tid / 4 of the tile, group tid % 4
+      const Philox4 w = dropout_words(dsp, qt * kTile + (tid >> 2), j0 / kTile, (uint32_t)bh, tid & 3);
+      uint32_t* z = &zbuf[buf][(tid >> 2) * kZRow + 4 * (tid & 3)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = w.x[e];
     }
   };
 
@@ -298,7 +335,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
     const lds_char* qt_l = qbase + par * Tile<DK>::BYTES;
     const lds_char* gt_l = gbase + par * Tile<DV>::BYTES;
     // no mask when every row of the tile exists and sees every key of the group
-    const bool masked = BIAS || q0 + kTile > Nq || key_last < j0 + kTile - 1 || (causal && q0 + shift < key_last);
+    const bool masked = BIAS || q0 + kTile > Nq || key_last < j0 + kTile - 1 || key_lo(mr, q0 + kTile - 1) > j0 ||
+                        key_end(mr, q0, klen) < j0 + kTile;
     // S and dP: row block rb, a lane holds rows 16rb + 4g + j of `key`
     f32x4 s[4], dp[4];
 #pragma unroll
@@ -321,9 +359,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
           arg = fmaf(bias[(bh * Nq + r) * (size_t)Nk + min(key, Nk - 1)], kLog2e, arg);
         }
         float p = fast_exp2(arg);
-        if (masked && key >= ebuf[par][rr]) p = 0.f;
-        pv[rb][j] = p;
-        dsv[rb][j] = p * (dp[rb][j] - cbuf[par][rr]);
+        if (masked && (unsigned)(key - lobuf[par][rr]) >= spbuf[par][rr]) p = 0.f;
+        float zr = 1.f;
+        if (DROP) {
+          // byte r16 % 4 of word `wave` of row rr's call for group r16 / 4
+          const uint32_t w = zbuf[par][rr * kZRow + 4 * (r16 >> 2) + wave];
+          zr = dropout_keep(w, r16 & 3, dsp.keep) ? drop_scale : 0.f;
+        }
+        pv[rb][j] = zr * p;
+        dsv[rb][j] = p * (zr * dp[rb][j] - cbuf[par][rr]);
       }
     }
     // dV^T += G^T P and dK^T += Q^T D over the tile's two 32-row steps
@@ -360,26 +404,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   }
 }
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
+  const KeyRange mr{a.off, a.wl, a.wr};
+  const DropoutSpec dsp{a.seed_lo, a.seed_hi, a.keep_256};
+  const float drop_scale = 256.f / (float)a.keep_256;
   const unsigned bh = (unsigned)(a.B * a.H);
   // dQ first: it stores c for the dK/dV kernel
   if ((long long)a.B * a.H * a.Nq > 0)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len,
-                       (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, a.causal);
+                       (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
   if (a.Nk > 0)
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS>), dim3((unsigned)((a.Nk + kTile - 1) / kTile), bh),
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nk + kTile - 1) / kTile), bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dk_out,
-                       (uint16_t*)a.dv_out, a.H, a.Nq, a.Nk, a.scale, a.causal);
+                       (uint16_t*)a.dv_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_b(const BwdArgs& a, hipStream_t s) {
-  return a.bias ? launch_t<DK, DV, true>(a, s) : launch_t<DK, DV, false>(a, s);
+  if (a.keep_256 < 256)
+    return a.bias ? launch_t<DK, DV, true, true>(a, s) : launch_t<DK, DV, false, true>(a, s);
+  return a.bias ? launch_t<DK, DV, true, false>(a, s) : launch_t<DK, DV, false, false>(a, s);
 }
 
 }  // namespace

@@ -43,7 +43,13 @@
 // work-group visits only the key tiles that meet the union of its rows'
 // ranges, and only tiles not inside every row's range of a wave are masked
 // element by element ([GS] section 6).
+//
+// Dropout (optional): P is dropped with the counter-based mask of
+// fa_dropout.h before the product with V; l sums the undropped P, and the
+// epilogue multiplies by 256/keep.  A lane holds four 4-key groups of its
+// row per 32 keys, one generator call each.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_mask.h"
 #include "launch.h"
 
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
     float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, KeyRange mr,
-    int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
+    DropoutSpec dsp, float drop_scale, int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
   using T = Tile<DK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF];
 
@@ -310,6 +316,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16x8 pb[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
+      // dropout: bit r of km keeps accumulator slot r (key n0 + 32kb +
+      // 8(r/4) + 4hf + r%4)
+      uint32_t km = 0xffffu;
+      if (dsp.keep < 256) {
+        km = 0u;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int j0 = n0 + kb * 32 + 8 * i4 + 4 * hf;
+          const uint32_t w = philox_word(dropout_words(dsp, qi, j0 >> 6, (uint32_t)bh, (j0 >> 2) & 3), (j0 >> 4) & 3);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) km |= dropout_keep(w, jj, dsp.keep) ? 1u << (4 * i4 + jj) : 0u;
+        }
+      }
       float xo[16];  // bias * log2e - m (bias path only)
       if (BIAS) {
 #pragma unroll
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           const float p0 = fast_exp2(BIAS ? s[kb][r0] + xo[r0] : fmaf(s[kb][r0], c, -m_use));
           const float p1 = fast_exp2(BIAS ? s[kb][r1] + xo[r1] : fmaf(s[kb][r1], c, -m_use));
           psum += p0 + p1;
-          w[e / 2] = pack_bf16x2(p0, p1);
+          w[e / 2] = pack_bf16x2((km >> r0) & 1u ? p0 : 0.f, (km >> r1) & 1u ? p1 : 0.f);
         }
         pb[kb * 2 + t2] = __builtin_bit_cast(bf16x8, w);
       }
@@ -361,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const float l_tot = half_swap_sum(l_run);
   if (!row_valid) return;
   const bool nonempty = l_tot > 0.f;
-  const float inv = nonempty ? 1.f / l_tot : 0.f;
+  const float inv = nonempty ? drop_scale / l_tot : 0.f;
   uint16_t* orow = o + (bh * Nq + qi) * (size_t)dv;
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) {
@@ -401,8 +420,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, BN, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
                      (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e,
-                     KeyRange{a.off, a.wl, a.wr},
-                     (int)vec_q, (int)vec_k, (int)vec_v, (int)vec_b, n_qt);
+                     KeyRange{a.off, a.wl, a.wr}, DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256},
+                     256.f / (float)a.keep_256, (int)vec_q, (int)vec_k, (int)vec_v, (int)vec_b, n_qt);
   return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@
 //   of its rows' ranges: a masked run along the left window edge, unmasked
 //   tiles inside every row's range, then a masked run along the right edge
 //   (the causal diagonal, the key-length boundary).
+// * Dropout (a separate instance): a lane's 16 keys of a row in a tile are
+//   exactly the 16 bytes of one counter-based generator call (fa_dropout.h),
+//   so each lane makes one call per query block and tile; dropped
+//   probabilities are zeroed in the bf16 P operand only (l sums the
+//   undropped ones) and the epilogue multiplies by 256/keep.
 //
 // Online state per query row (base-2 domain): reference m (moved lazily,
 // only when the tile maximum exceeds it by more than 8), denominator l and
@@ -56,6 +61,7 @@
 // is divided once at the end ([GS] section 5).  Rows with no allowed key keep
 // m = -inf and produce o = 0, lse = -inf ([GS] section 6).
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_mask.h"
 #include "launch.h"
 
@@ -269,11 +275,12 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&p
 // Softmax of one tile in place: mask, running reference, exponentials and P
 // in bf16.  alpha[qb] receives the factor the value sums must be multiplied
 // by; the return value says whether any row of the wave moved its reference.
-template <bool MASK, bool BIAS>
+template <bool MASK, bool BIAS, bool DROP>
 __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2], RowState& st, float (&alpha)[2],
                                              float c, int n0, const int (&row_lo)[2],
                                              const unsigned (&row_span)[2], const float* const (&brow)[2],
-                                             const bool (&rvalid)[2], int nk, bool vec_bias, int g) {
+                                             const bool (&rvalid)[2], int nk, bool vec_bias, int g,
+                                             const Philox4 (&zw)[2], int keep) {
   float xo[2][4][4];  // bias path: the raw bias per element
   float mx[2];
 #pragma unroll
@@ -332,6 +339,12 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
           p[j] = fast_exp2(arg);
         }
         psum += (p[0] + p[1]) + (p[2] + p[3]);
+        if (DROP) {
+          // word kb of the query block's generator call: byte j keeps key 16kb + 4g + j
+          const uint32_t zb = zw[qb].x[kb];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[j] = dropout_keep(zb, j, keep) ? p[j] : 0.f;
+        }
         w[2 * h] = cvt_pk_bf16(p[0], p[1]);
         w[2 * h + 1] = cvt_pk_bf16(p[2], p[3]);
       }
@@ -342,7 +355,7 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
   return __builtin_amdgcn_ballot_w64(any_grow) != 0;
 }
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 struct FwdTile {
   // inputs of this work-group
   const uint16_t* kbh;
@@ -352,6 +365,8 @@ struct FwdTile {
   int qrow0;    // global index of this lane's row in query block 0 (block 1: +16)
   int klen;     // keys of this sequence
   KeyRange mr;  // position masks; row ranges are rebuilt only for masked tiles
+  DropoutSpec dsp;  // DROP only
+  uint32_t bh;      // b*H + h, a dropout counter word
   bool rvalid[2];
   const float* brow[2];
   int vec_bias, g;
@@ -384,10 +399,15 @@ struct FwdTile {
         row_span[qb] = end > lo ? (unsigned)(end - lo) : 0u;
       }
     }
+    Philox4 zw[2];
+    if (DROP) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) zw[qb] = dropout_words(dsp, qrow0 + 16 * qb, t, bh, g);
+    }
     bf16x8 pb[2][2];
     float alpha[2];
-    const bool grow =
-        softmax_tile<MASK, BIAS>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk, vec_bias != 0, g);
+    const bool grow = softmax_tile<MASK, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
+                                                     vec_bias != 0, g, zw, dsp.keep);
     if (grow) {
 #pragma unroll
       for (int d = 0; d < DV / 16; ++d) {
@@ -401,11 +421,12 @@ struct FwdTile {
   }
 };
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int H, int Nq, int Nk, float scale_log2, KeyRange mr, int vec_bias, int n_qt) {
+    float* __restrict__ lse, int H, int Nq, int Nk, float scale_log2, KeyRange mr, DropoutSpec dsp,
+    float drop_scale, int vec_bias, int n_qt) {
   __shared__ __attribute__((aligned(1024))) char kbuf0[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[SwzTile<DV>::BYTES];
@@ -435,7 +456,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
 
-  FwdTile<DK, DV, BIAS> ft;
+  FwdTile<DK, DV, BIAS, DROP> ft;
+  ft.dsp = dsp;
+  ft.bh = (uint32_t)tc.bh;
   ft.kbh = k + bh * Nk * DK;
   ft.vbh = v + bh * Nk * DV;
   ft.nk = Nk;
@@ -532,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     const float l_tot = quad_sum(ft.st.l[qb]);
     if (!ft.rvalid[qb]) continue;
     const bool nonempty = l_tot > 0.f;
-    const float inv = nonempty ? 1.f / l_tot : 0.f;
+    const float inv = nonempty ? (DROP ? drop_scale : 1.f) / l_tot : 0.f;
     uint16_t* orow = o + (bh * Nq + qrow[qb]) * (size_t)DV;
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
@@ -547,23 +570,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   }  // pass
 }
 
-template <int DK, int DV, bool BIAS>
+template <int DK, int DV, bool BIAS, bool DROP>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const bool pair = FA_FAST_PAIR && a.wl < 0 && a.wr == 0;
   const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
   const long long total = (long long)n_units * a.H * a.B;
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & 15) == 0);
-  hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
                      (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr},
-                     (int)vec_b, n_qt);
+                     DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256}, 256.f / (float)a.keep_256, (int)vec_b, n_qt);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_b(const FwdArgs& a, hipStream_t s) {
-  return a.bias ? launch_t<DK, DV, true>(a, s) : launch_t<DK, DV, false>(a, s);
+  if (a.keep_256 < 256)
+    return a.bias ? launch_t<DK, DV, true, true>(a, s) : launch_t<DK, DV, false, true>(a, s);
+  return a.bias ? launch_t<DK, DV, true, false>(a, s) : launch_t<DK, DV, false, false>(a, s);
 }
 
 }  // namespace

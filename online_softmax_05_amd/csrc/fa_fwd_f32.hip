@@ -22,7 +22,12 @@
 // work-group visits only the key tiles that meet the union of its rows'
 // ranges, and only tiles not inside every row's range of a wave are masked
 // element by element ([GS] section 6).
+//
+// Dropout (optional): P is dropped with the counter-based mask of
+// fa_dropout.h before the product with V; l sums the undropped P, and the
+// epilogue multiplies by 256/keep.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_mask.h"
 #include "launch.h"
 
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, float* __restrict__ o,
     float* __restrict__ lse, int H, int Nq, int Nk, int dk, int dv, float scale_log2, KeyRange mr,
-    int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
+    DropoutSpec dsp, float drop_scale, int vec_q, int vec_k, int vec_v, int vec_bias, int n_qt) {
   using T = TileF<DK, DV, BN>;
   __shared__ __attribute__((aligned(16))) float smem[T::K_ELEMS + T::V_ELEMS];
   float* ks = smem;
@@ -189,11 +194,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
       for (int i = 0; i < 4; ++i) {
         f32x4 bv = {0.f, 0.f, 0.f, 0.f};
         if (BIAS) bv = load_bias4(brow, n0 + kb * 32 + 8 * i + 4 * hf, Nk, vec_bias != 0, row_valid);
+        // dropout word of keys n0 + 32kb + 8i + 4hf .. +3 (all kept without dropout)
+        uint32_t zw = 0u;
+        if (dsp.keep < 256) {
+          const int j0 = n0 + kb * 32 + 8 * i + 4 * hf;
+          zw = philox_word(dropout_words(dsp, qi, j0 >> 6, (uint32_t)bh, (j0 >> 2) & 3), (j0 >> 4) & 3);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float off = BIAS ? fmaf(bv[j], kLog2e, -m_use) : -m_use;
           const float p = fast_exp2(s[kb][4 * i + j] + off);
-          s[kb][4 * i + j] = p;
+          s[kb][4 * i + j] = dropout_keep(zw, j, dsp.keep) ? p : 0.f;
           psum += p;
         }
       }
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   const float l_tot = half_swap_sum(l_run);
   if (!row_valid) return;
   const bool nonempty = l_tot > 0.f;
-  const float inv = nonempty ? 1.f / l_tot : 0.f;
+  const float inv = nonempty ? drop_scale / l_tot : 0.f;
   float* orow = o + (bh * Nq + qi) * (size_t)dv;
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) {
@@ -258,7 +269,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & m16) == 0);
   hipLaunchKernelGGL((fwd_f32_kernel<DK, DV, BN, BIAS>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, a.bias, a.k_len, (float*)a.o,
-                     a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr}, (int)vec_q, (int)vec_k,
+                     a.lse, a.H, a.Nq, a.Nk, a.dk, a.dv, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr},
+                     DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256}, 256.f / (float)a.keep_256, (int)vec_q, (int)vec_k,
                      (int)vec_v, (int)vec_b, n_qt);
   return hipGetLastError();
 }

@@ -24,6 +24,9 @@ struct FwdArgs {
   int off;
   int wl;
   int wr;
+  // dropout of P (fa_dropout.h): keep_256 == 256 means none
+  int keep_256;
+  uint32_t seed_lo, seed_hi;
 };
 
 struct DecodeArgs {
@@ -55,7 +58,13 @@ struct BwdArgs {
   float* ws_c;  // [B*H*Nq]: c_i = dO_i . O_i
   int B, H, Nq, Nk, dk, dv;
   float scale;
-  int causal;
+  int causal;  // unused by the kernels: the position masks below include it
+  // position masks as for the forward (fa_mask.h) and dropout (fa_dropout.h)
+  int off;
+  int wl;
+  int wr;
+  int keep_256;
+  uint32_t seed_lo, seed_hi;
 };
 
 struct DecodeMqArgs {

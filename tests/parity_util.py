@@ -36,7 +36,8 @@ def oracle_full(inp):
     return oracle.attention_ref(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), scale=scale32(inp["scale"]),
                                 causal=inp["causal"], k_len=k_len, bias=f64(inp.get("bias")),
                                 align=inp.get("align", "bottom_right"),
-                                window=(inp.get("window_left"), inp.get("window_right")))
+                                window=(inp.get("window_left"), inp.get("window_right")),
+                                dropout=inp.get("dropout"))
 
 
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None, logit_scale=1.0):
@@ -68,7 +69,7 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, empty=None, logit_scale
 
 
 def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None, align="bottom_right",
-                window=(None, None)):
+                window=(None, None), dropout=None):
     """Oracle on sampled rows of device tensors: rows is a list of (b, h, i).
     Only the needed slices are copied to the host.  Returns (o [n, dv], lse [n])."""
     B, H, Nq, _ = q.shape
@@ -86,7 +87,7 @@ def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None, align="b
         bb = None if bias is None else f64(bias[b, h, idx])
         ob, lb = oracle.attention_head(qi, kk, vv, scale=scale32(scale), nq=Nq, causal=causal,
                                        k_len_b=None if kl is None else int(kl[b]), bias=bb, row_ids=idx,
-                                       align=align, window=window)
+                                       align=align, window=window, dropout=dropout, bh=b * H + h)
         for j, (n, _) in enumerate(items):
             o[n] = ob[j]
             lse[n] = lb[j]

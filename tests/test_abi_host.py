@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert {"fa_fwd", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes", "fa_check_fwd",
             "fa_check_decode", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd", "fa_status_str",
             "fa_abi_version", "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes",
-            "fa_check_decode_mq", "fa_fwd_ex", "fa_check_fwd_ex"} <= set(names)
+            "fa_check_decode_mq", "fa_fwd_ex", "fa_check_fwd_ex", "fa_bwd_ex", "fa_check_bwd_ex"} <= set(names)
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
@@ -60,7 +60,7 @@ def test_header_is_plain_c():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 103
+    assert fa.fa_abi_version() == 104
     for st in range(6):
         assert isinstance(fa.fa_status_str(st), str) and fa.fa_status_str(st)
     assert fa.fa_status_str(0) == "ok"
@@ -106,11 +106,11 @@ def test_check_fwd(kw, want):
     assert check_fwd(**kw) == want
 
 
-def check_fwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, **kw):
+def check_fwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, keep=256, seed=0, **kw):
     a = fwd_args(**kw)
     return fa.fa_check_fwd_ex(a["q"], a["k"], a["v"], a["bias"], a["k_len"], a["o"], a["lse"], a["B"],
                               a["H"], a["Nq"], a["Nk"], a["dk"], a["dv"], a["dtype"], a["scale"], a["causal"],
-                              align, wl, wr, a["block_n"])
+                              align, wl, wr, keep, seed, a["block_n"])
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -119,19 +119,47 @@ def check_fwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, **kw):
     ({"wl": -2}, UNSUP), ({"wr": -7}, UNSUP),
     ({"wl": 4, "dk": 300}, UNSUP), ({"wl": 4, "q": None}, NULL), ({"wl": 4, "causal": 3}, UNSUP),
     ({"wl": 4, "Nq": 0, "q": None, "o": None}, OK),
+    ({"keep": 230, "seed": 2**64 - 1}, OK), ({"keep": 1}, OK), ({"keep": 0}, UNSUP), ({"keep": 257}, UNSUP),
+    ({"keep": -3}, UNSUP), ({"keep": 200, "wl": 7, "align": fa.FA_ALIGN_TOP_LEFT, "dtype": fa.FA_F32}, OK),
 ])
 def test_check_fwd_ex(kw, want):
     assert check_fwd_ex(**kw) == want
 
 
 def test_fwd_ex_rejects_before_launch():
-    st = fa.lib().fa_fwd_ex(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 5, -1, -1, 0, None)
-    assert st == UNSUP
-    st = fa.lib().fa_fwd_ex(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 0, -3, -1, 0, None)
-    assert st == UNSUP
-    st = fa.lib().fa_fwd_ex(None, None, None, None, None, None, None, 0, 4, 4, 4, 8, 8, fa.FA_F32, 1.0, 0, 1, 3,
-                            3, 0, None)
-    assert st == OK
+    f = fa.lib().fa_fwd_ex
+    assert f(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 5, -1, -1, 256, 0, 0, None) == UNSUP
+    assert f(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 0, -3, -1, 256, 0, 0, None) == UNSUP
+    assert f(P, P, P, None, None, P, P, 1, 1, 4, 4, 8, 8, fa.FA_BF16, 1.0, 1, 0, -1, -1, 0, 7, 0, None) == UNSUP
+    assert f(None, None, None, None, None, None, None, 0, 4, 4, 4, 8, 8, fa.FA_F32, 1.0, 0, 1, 3, 3, 100, 9, 0,
+             None) == OK
+
+
+def test_keep_256_for():
+    assert fa.keep_256_for(0.0) == 256 and fa.keep_256_for(0.1) == 230 and fa.keep_256_for(0.5) == 128
+    assert fa.keep_256_for(0.999) == 1
+    for bad in (-0.1, 1.0, 2.0):
+        with pytest.raises(fa.FaError):
+            fa.keep_256_for(bad)
+
+
+def check_bwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, keep=256, **kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, bias=None, k_len=None, dq=P, dk=P, dv=P, B=2, H=3, Nq=40, Nk=70,
+             d_k=64, d_v=64, dtype=fa.FA_BF16, scale=0.125, causal=1)
+    a.update(kw)
+    ws = fa.fa_bwd_workspace_bytes(a["B"], a["H"], a["Nq"])
+    return fa.fa_check_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["bias"], a["k_len"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d_k"], a["d_v"], a["dtype"],
+                              a["scale"], a["causal"], align, wl, wr, keep, 5, P, ws)
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, OK), ({"align": fa.FA_ALIGN_TOP_LEFT, "wl": 3}, OK), ({"keep": 100}, OK), ({"keep": 0}, UNSUP),
+    ({"keep": 300}, UNSUP), ({"align": 7}, UNSUP), ({"wr": -2}, UNSUP), ({"q": None}, NULL), ({"causal": 5}, UNSUP),
+    ({"d_k": 200}, UNSUP),
+])
+def test_check_bwd_ex(kw, want):
+    assert check_bwd_ex(**kw) == want
 
 
 def test_fwd_rejects_before_launch():
