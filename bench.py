@@ -56,21 +56,30 @@ METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s (% peak)"
 # summaries are only reported while these still hash to the recorded value)
 KERNEL_SOURCES = {
     "prefill": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
-                "online_softmax_05_amd/csrc/fa_mask.h"],
+                "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
     "long": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
-             "online_softmax_05_amd/csrc/fa_mask.h"],
+             "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
     "window": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
-               "online_softmax_05_amd/csrc/fa_mask.h"],
+               "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
+    "dropout": ["online_softmax_05_amd/csrc/fa_fwd_bf16_fast.hip", "online_softmax_05_amd/csrc/fa_common.h",
+                "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
+    "dropout_bwd": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
+                    "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h",
+                    "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
     "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
     "backward": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
-                 "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h"],
+                 "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h",
+                 "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
     "decode_mq": ["online_softmax_05_amd/csrc/fa_decode_mq.hip", "online_softmax_05_amd/csrc/fa_tiles.h",
                   "online_softmax_05_amd/csrc/fa_common.h"],
 }
-KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false>", "long": "fwd_bf16_fast_kernel<128, 128, false>",
-                "window": "fwd_bf16_fast_kernel<128, 128, false>",
+KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false>",
+                "long": "fwd_bf16_fast_kernel<128, 128, false, false>",
+                "window": "fwd_bf16_fast_kernel<128, 128, false, false>",
+                "dropout": "fwd_bf16_fast_kernel<128, 128, false, true>",
+                "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true> + bwd_dkdv_bf16_kernel<128, 128, false, true>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
-                "backward": "bwd_dq_bf16_kernel<128, 128, false> + bwd_dkdv_bf16_kernel<128, 128, false>",
+                "backward": "bwd_dq_bf16_kernel<128, 128, false, false> + bwd_dkdv_bf16_kernel<128, 128, false, false>",
                 "decode_mq": "mq_partial_bf16_kernel + mq_merge_kernel"}
 
 
@@ -169,7 +178,8 @@ def cpu_baseline_prefill(inp, name, budget_s):
         for r0 in range(0, N, 2048):
             r1 = min(N, r0 + 2048)
             oracle.attention_head(qh[r0:r1], kh, vh, scale=scale, nq=N, causal=True,
-                                  row_ids=np.arange(r0, r1), window=(wl, None))
+                                  row_ids=np.arange(r0, r1), window=(wl, None), dropout=inp.get("dropout"),
+                                  bh=bh)
         elapsed += time.perf_counter() - ts
         flops += 2.0 * (dk + dv) * causal_pairs(N, N, wl)
         heads += 1
@@ -230,14 +240,15 @@ def run_prefill(name, args, dev):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
     wl = inp.get("window_left")
+    keep, seed = inp.get("dropout") or (256, 0)
 
     def step():
-        if wl is None:
+        if wl is None and keep == 256:
             fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"],
                       out=out, lse=lse)
         else:
             fa.fa_fwd_ex(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, window_left=wl,
-                         block_n=inp["block_n"], out=out, lse=lse)
+                         keep_256=keep, seed=seed, block_n=inp["block_n"], out=out, lse=lse)
 
     log(f"{name}: timing {args.warmup} + {args.steps} steps")
     t = time_launches(step, args.steps, args.warmup)
@@ -257,7 +268,8 @@ def run_prefill(name, args, dev):
                       + 4 * B * H * N),
         config=dict(workload=workloads.DESCRIPTIONS[name], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
                     dtype="bf16", block_n=64 if inp["block_n"] == 0 else inp["block_n"],
-                    allowed_pairs=pairs, **({} if wl is None else {"window_left": wl})),
+                    allowed_pairs=pairs, **({} if wl is None else {"window_left": wl}),
+                    **({} if keep == 256 else {"dropout_keep_256": keep, "dropout_seed": seed})),
     )
     if not args.no_cpu_baseline:
         log(f"{name}: timing the oracle on a bounded sample")
@@ -268,7 +280,7 @@ def run_prefill(name, args, dev):
     return res
 
 
-def cpu_baseline_backward(inp, budget_s):
+def cpu_baseline_backward(inp, budget_s, name="backward"):
     import numpy as np
 
     import oracle
@@ -284,55 +296,61 @@ def cpu_baseline_backward(inp, budget_s):
         b, h = divmod(bh, H)
         qh, kh, vh, gh = (t[b, h].double().cpu().numpy() for t in (q, k, v, g))
         ts = time.perf_counter()
-        oracle.attention_bwd_head(qh, kh, vh, gh, scale=scale, nq=N, causal=True)
+        oracle.attention_bwd_head(qh, kh, vh, gh, scale=scale, nq=N, causal=True, dropout=inp.get("dropout"), bh=bh)
         elapsed += time.perf_counter() - ts
         flops += 2.0 * (3 * dk + 2 * dv) * causal_pairs(N, N)
         heads += 1
         if elapsed >= budget_s:
             break
     return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
-                sample=f"{heads} of {B * H} heads of the backward workload, dense float64 numpy oracle "
+                sample=f"{heads} of {B * H} heads of the {name} workload, dense float64 numpy oracle "
                        f"(forward included), {elapsed:.1f} s of oracle time (input copies excluded)",
                 seconds=elapsed, cpu=platform.processor() or platform.machine())
 
 
-def run_backward(args, dev):
+def run_backward(args, dev, name="backward"):
     import torch
 
     import online_softmax_05_amd as fa
     import workloads
 
-    log("backward: drawing inputs on the device")
-    inp = workloads.backward(dev)
-    s = workloads.SHAPES["backward"]
+    log(f"{name}: drawing inputs on the device")
+    inp = getattr(workloads, name)(dev)
+    s = workloads.SHAPES[name]
     B, H, N, dk, dv = s["B"], s["H"], s["Nq"], s["dk"], s["dv"]
-    o, lse = fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True)
+    keep, seed = inp.get("dropout") or (256, 0)
+    o, lse = fa.fa_fwd_ex(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, keep_256=keep, seed=seed)
     dq, dk_, dv_ = torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"])
     ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32, device=dev)
 
     def step():
-        fa.fa_bwd(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True, dq=dq, dk=dk_,
-                  dv=dv_, workspace=ws)
+        if keep == 256:
+            fa.fa_bwd(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True, dq=dq,
+                      dk=dk_, dv=dv_, workspace=ws)
+        else:
+            fa.fa_bwd_ex(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True,
+                         keep_256=keep, seed=seed, dq=dq, dk=dk_, dv=dv_, workspace=ws)
 
-    log(f"backward: timing {args.warmup} + {args.steps} steps")
+    log(f"{name}: timing {args.warmup} + {args.steps} steps")
     t = time_launches(step, args.steps, args.warmup)
     pairs = B * H * causal_pairs(N, N)
     flops = 2.0 * (3 * dk + 2 * dv) * pairs
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (t["launch_ms_mean"] * 1e-3) / 1e12
     res = dict(
-        workload=workloads.DESCRIPTIONS["backward"], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
+        workload=workloads.DESCRIPTIONS[name], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_BF16_TFLOPS,
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=stored_traffic("backward"),
-                      kernel=KERNEL_NAMES["backward"], launch_ms_mean=t["launch_ms_mean"],
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=stored_traffic(name),
+                      kernel=KERNEL_NAMES[name], launch_ms_mean=t["launch_ms_mean"],
                       launch_ms_median=t["launch_ms_median"], algorithmic_flops_per_launch=flops),
-        config=dict(workload=workloads.DESCRIPTIONS["backward"], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
-                    dtype="bf16", allowed_pairs=pairs),
+        config=dict(workload=workloads.DESCRIPTIONS[name], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
+                    dtype="bf16", allowed_pairs=pairs,
+                    **({} if keep == 256 else {"dropout_keep_256": keep, "dropout_seed": seed})),
     )
     if not args.no_cpu_baseline:
-        log("backward: timing the oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline_backward(inp, args.cpu_budget)
+        log(f"{name}: timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_backward(inp, args.cpu_budget, name)
     del inp, o, lse, dq, dk_, dv_, ws
     torch.cuda.empty_cache()
     return res
@@ -441,8 +459,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["prefill", "long", "decode", "decode_mq", "backward", "window"],
-                    default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "decode", "decode_mq", "backward", "window",
+                                           "dropout", "dropout_bwd"], default="prefill")
     ap.add_argument("--only", action="store_true", help="measure only the main workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -468,8 +486,10 @@ def main():
         return
 
     order = [args.workload] + ([] if args.only else [w for w in ("prefill", "long", "decode", "decode_mq", "backward",
-                                                                  "window") if w != args.workload])
-    runners = {"decode": run_decode, "decode_mq": run_decode_mq, "backward": run_backward}
+                                                                  "window", "dropout", "dropout_bwd")
+                                                      if w != args.workload])
+    runners = {"decode": run_decode, "decode_mq": run_decode_mq, "backward": run_backward,
+               "dropout_bwd": lambda a, d: run_backward(a, d, "dropout_bwd")}
     results = {}
     for w in order:
         results[w] = runners[w](args, dev) if w in runners else run_prefill(w, args, dev)

@@ -26,6 +26,9 @@ Workloads (sizes as [B, H, N, d]):
                   ~ N(0,1) from seed 203.
 * ``window``      the prefill Q, K, V with a causal sliding window of 1024
                   keys (each row sees its own position and the 1023 before).
+* ``dropout``     the prefill Q, K, V with dropout p = 0.1 (keep 230 of 256
+                  byte values), mask seed 0x5EED.
+* ``dropout_bwd`` the backward workload under that same dropout.
 
 Workload k draws Q/K/V from seed k; bias, k_len and the special rows come
 from a second generator seeded 100 + k.  Small workloads are drawn on the CPU
@@ -49,6 +52,8 @@ SHAPES = {
     "backward": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
     "decode_mq": dict(B=64, H=32, Nq=4, Nk=8192, dk=128, dv=128),
     "window": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
+    "dropout": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
+    "dropout_bwd": dict(B=4, H=32, Nq=4096, Nk=4096, dk=128, dv=128),
 }
 
 DESCRIPTIONS = {
@@ -61,7 +66,11 @@ DESCRIPTIONS = {
     "decode_mq": "split-K multi-query decode 64x32 sequences x 4 query rows (causal), KV lengths U[1,8192], d128 bf16, "
                  "512-key chunks",
     "window": "attention fwd prefill 4x32x4096x4096 d128 bf16 causal, sliding window of 1024 keys",
+    "dropout": "attention fwd prefill 4x32x4096x4096 d128 bf16 causal, dropout p=0.1 (keep 230/256)",
+    "dropout_bwd": "attention bwd 4x32x4096x4096 d128 bf16 causal, dropout p=0.1 (keep 230/256) replayed",
 }
+
+DROPOUT = (230, 0x5EED)  # (keep_256, seed) of the dropout workloads
 
 
 def _randn_cpu(gen, shape, std=1.0):
@@ -125,6 +134,21 @@ def window(device):
     sliding window of 1024 keys (left width 1023)."""
     inp = prefill(device)
     inp["window_left"] = 1023
+    return inp
+
+
+def dropout(device):
+    """The prefill workload's Q, K, V (same seed, same draws) with dropout
+    (keep_256, seed) = DROPOUT."""
+    inp = prefill(device)
+    inp["dropout"] = DROPOUT
+    return inp
+
+
+def dropout_bwd(device):
+    """The backward workload under the dropout workload's mask."""
+    inp = backward(device)
+    inp["dropout"] = DROPOUT
     return inp
 
 
