@@ -172,8 +172,10 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   if (d_k > kMaxHeadDim || d_v > kMaxHeadDim) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
-  // grids are (row or key tiles, B*H): the second grid dimension is 16-bit
+  // general kernels: grids (row or key tiles, B*H) with a 16-bit second
+  // dimension; matrix-core kernels: one dimension of tiles * B * H
   if (!product_fits({B, H}, 65535)) return FA_ERR_SHAPE;
+  if (!product_fits({(std::max(Nq, Nk) + 63LL) / 64, B, H}, kInt32Max)) return FA_ERR_SHAPE;
   if (Nq > kInt32Max - Nk) return FA_ERR_SHAPE;
   const long long bhq = (long long)B * H * Nq, bhk = (long long)B * H * Nk;
   if (bhq == 0 && bhk == 0) return FA_OK;  // nothing to compute

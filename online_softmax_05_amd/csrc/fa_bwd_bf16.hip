@@ -32,6 +32,12 @@
 // P and D are rounded to bf16 only as matrix-core operands; every sum is
 // fp32.
 //
+// Both grids are one-dimensional and XCD-aware (map_tile): the 8 XCDs each
+// take a contiguous range of (batch*head, tile) work-groups, so the tiles of
+// one head that run at the same time share an L2 and its re-read K/V (dQ) or
+// Q/dO (dK/dV) tiles; the dQ kernel issues a head's causal tiles heaviest
+// first.
+//
 // Position masks are the forward's visible key range [lo, end) per row
 // (fa_mask.h); both kernels visit only tiles that meet some row's range and
 // test elements only on edge tiles.  Dropout (a separate instance; [GS]
@@ -108,9 +114,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const size_t bh = blockIdx.y;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, (Nq + kTile - 1) / kTile, mr.wr >= 0);
+  const size_t bh = (size_t)tc.bh;
   const int b = (int)(bh / H);
-  const int q0 = blockIdx.x * kTile;
+  const int q0 = tc.qt * kTile;
   const int klen = clamp_klen(k_len, b, Nk);
   const int row = q0 + 16 * wave + r16;  // this lane's query row
   const bool rvalid = row < Nq;
@@ -259,9 +266,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const size_t bh = blockIdx.y;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, (Nk + kTile - 1) / kTile, false);
+  const size_t bh = (size_t)tc.bh;
   const int b = (int)(bh / H);
-  const int j0 = blockIdx.x * kTile;
+  const int j0 = tc.qt * kTile;
   const int klen = clamp_klen(k_len, b, Nk);
   const int key = j0 + 16 * wave + r16;  // this lane's key
   const bool kvalid = key < Nk;
@@ -412,12 +420,12 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   // dQ first: it stores c for the dK/dV kernel
   if ((long long)a.B * a.H * a.Nq > 0)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kTile - 1) / kTile), bh),
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kTile - 1) / kTile) * bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len,
                        (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
   if (a.Nk > 0)
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nk + kTile - 1) / kTile), bh),
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nk + kTile - 1) / kTile) * bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len, (uint16_t*)a.dk_out,
                        (uint16_t*)a.dv_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
