@@ -15,8 +15,10 @@
 // follows on the same stream.  Neither uses atomics, so the results are
 // bitwise reproducible.
 //
-// dQ kernel: one work-group = 4 waves = 64 query rows of one (batch, head),
-// 16 rows per wave with their Q and G rows held as MFMA operands.  Key tiles
+// dQ kernel: one work-group = 4 waves = 128 query rows of one (batch, head),
+// 32 rows per wave (two 16-row blocks, so that every K or V fragment read
+// from LDS feeds two products) with their Q and G rows held as MFMA
+// operands.  Key tiles
 // of 64 keys stream through LDS (direct-to-LDS loads, double buffered), and
 // per tile each wave forms
 //   S^T  = K Q^T     (v_mfma_f32_16x16x32_bf16; a lane holds 4 keys of one row)
@@ -98,6 +100,8 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
 // dQ
 // ---------------------------------------------------------------------------
 
+constexpr int kDqRows = 32 * kWaves;  // query rows per dQ work-group (32 per wave)
+
 template <int DK, int DV, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -114,13 +118,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, (Nq + kTile - 1) / kTile, mr.wr >= 0);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, (Nq + kDqRows - 1) / kDqRows, mr.wr >= 0);
   const size_t bh = (size_t)tc.bh;
   const int b = (int)(bh / H);
-  const int q0 = tc.qt * kTile;
+  const int q0 = tc.qt * kDqRows;
   const int klen = clamp_klen(k_len, b, Nk);
-  const int row = q0 + 16 * wave + r16;  // this lane's query row
-  const bool rvalid = row < Nq;
 
   TileAddr<DK> ka;
   TileAddr<DV> va;
@@ -128,41 +130,58 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   va.init(lane, wave);
   const uint16_t* kbh = k + bh * Nk * DK;
   const uint16_t* vbh = v + bh * Nk * DV;
-
-  bf16x8 qf[DK / 32], gf[DV / 32];
-  load_rows_b<DK>(qf, q + bh * Nq * DK, row, rvalid, g);
-  load_rows_b<DV>(gf, dout + bh * Nq * DV, row, rvalid, g);
-  const float l_row = rvalid ? lse[bh * Nq + row] : kNegInf;
-  const bool live = l_row != kNegInf;  // rows without an allowed key contribute nothing
-  const float l2 = live ? l_row * kLog2e : 0.f;
-  // c_i = g_i . o_i: this lane's quarter of the row (dims 32t + 8g .. +7),
-  // then the four lanes r16, r16 + 16, r16 + 32, r16 + 48 of the row
-  float c_row = 0.f;
-  {
-    bf16x8 of[DV / 32];
-    load_rows_b<DV>(of, o + bh * Nq * DV, row, rvalid, g);
-#pragma unroll
-    for (int t = 0; t < DV / 32; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c_row = fmaf((float)gf[t][e], (float)of[t][e], c_row);
-    c_row += __shfl_xor(c_row, 16);
-    c_row += __shfl_xor(c_row, 32);
-    if (rvalid && g == 0) cvec[bh * Nq + row] = c_row;
-  }
   const float c2 = scale * kLog2e;
-  // this row's visible keys [row_lo, row_lo + row_span) (none for a dead row)
-  const int row_lo = key_lo(mr, row);
-  const int row_end = live ? key_end(mr, row, klen) : 0;
-  const unsigned row_span = row_end > row_lo ? (unsigned)(row_end - row_lo) : 0u;
-  const float* brow = BIAS ? bias + (bh * Nq + (size_t)(rvalid ? row : 0)) * Nk : nullptr;
 
-  f32x4 acc[DK / 16];
+  // Each wave holds 32 query rows as two 16-row blocks qb: every K or V
+  // fragment read from LDS feeds both blocks' products.  Per block: the Q
+  // and G rows as B operands, L log2 e, c, the visible key range.
+  int row[2];
+  bool rvalid[2], live[2];
+  bf16x8 qf[2][DK / 32], gf[2][DV / 32];
+  float l2[2], c_row[2];
+  int row_lo[2];
+  unsigned row_span[2];
+  const float* brow[2];
 #pragma unroll
-  for (int d = 0; d < DK / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < 2; ++qb) {
+    row[qb] = q0 + 32 * wave + 16 * qb + r16;
+    rvalid[qb] = row[qb] < Nq;
+    load_rows_b<DK>(qf[qb], q + bh * Nq * DK, row[qb], rvalid[qb], g);
+    load_rows_b<DV>(gf[qb], dout + bh * Nq * DV, row[qb], rvalid[qb], g);
+    const float l_row = rvalid[qb] ? lse[bh * Nq + row[qb]] : kNegInf;
+    live[qb] = l_row != kNegInf;  // rows without an allowed key contribute nothing
+    l2[qb] = live[qb] ? l_row * kLog2e : 0.f;
+    // c_i = g_i . o_i: this lane's quarter of the row (dims 32t + 8g .. +7),
+    // then the four lanes r16, r16 + 16, r16 + 32, r16 + 48 of the row
+    float cr = 0.f;
+    {
+      bf16x8 of[DV / 32];
+      load_rows_b<DV>(of, o + bh * Nq * DV, row[qb], rvalid[qb], g);
+#pragma unroll
+      for (int t = 0; t < DV / 32; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cr = fmaf((float)gf[qb][t][e], (float)of[t][e], cr);
+      cr += __shfl_xor(cr, 16);
+      cr += __shfl_xor(cr, 32);
+      if (rvalid[qb] && g == 0) cvec[bh * Nq + row[qb]] = cr;
+    }
+    c_row[qb] = cr;
+    // this row's visible keys [row_lo, row_lo + row_span) (none for a dead row)
+    row_lo[qb] = key_lo(mr, row[qb]);
+    const int end = live[qb] ? key_end(mr, row[qb], klen) : 0;
+    row_span[qb] = end > row_lo[qb] ? (unsigned)(end - row_lo[qb]) : 0u;
+    brow[qb] = BIAS ? bias + (bh * Nq + (size_t)(rvalid[qb] ? row[qb] : 0)) * Nk : nullptr;
+  }
+
+  f32x4 acc[2][DK / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int d = 0; d < DK / 16; ++d) acc[qb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // key tiles that meet the union of the rows' ranges; tiles in
   // [t_full, t_full_end) lie inside every row's range and need no mask
-  const int last_row = min(q0 + kTile, Nq) - 1;
+  const int last_row = min(q0 + kDqRows, Nq) - 1;
   const int kbeg = key_lo(mr, q0);
   const int kend = key_end(mr, last_row, klen);
   const int t_begin = kbeg / kTile;
@@ -187,53 +206,73 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     }
     const lds_char* kt = kbase + par * Tile<DK>::BYTES;
     const lds_char* vt = vbase + par * Tile<DV>::BYTES;
-    const bool masked = t < t_full || t >= t_full_end || !live || BIAS;
-    // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of `row`
-    f32x4 s[4], dp[4];
+    const bool tile_masked = t < t_full || t >= t_full_end || BIAS;
+    // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of row[qb]
+    f32x4 s[4][2], dp[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < DK / 32; ++i) s[kb] = mfma(frag_read(kt + ka.frag[i] + 16 * kb * Tile<DK>::ROW), qf[i], s[kb]);
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = dp[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < DV / 32; ++i) dp[kb] = mfma(frag_read(vt + va.frag[i] + 16 * kb * Tile<DV>::ROW), gf[i], dp[kb]);
+      for (int i = 0; i < DK / 32; ++i) {
+        const bf16x8 a = frag_read(kt + ka.frag[i] + 16 * kb * Tile<DK>::ROW);
+        s[kb][0] = mfma(a, qf[0][i], s[kb][0]);
+        s[kb][1] = mfma(a, qf[1][i], s[kb][1]);
+      }
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i) {
+        const bf16x8 a = frag_read(vt + va.frag[i] + 16 * kb * Tile<DV>::ROW);
+        dp[kb][0] = mfma(a, gf[0][i], dp[kb][0]);
+        dp[kb][1] = mfma(a, gf[1][i], dp[kb][1]);
+      }
     }
-    // P^T and D^T = P^T o (dP^T - c)   (dropout: P^T o (z r dP^T - c))
-    Philox4 zw;
-    if (DROP) zw = dropout_words(dsp, row, t, (uint32_t)bh, g);
-    f32x4 dsv[4];
+    // P^T and D^T = P^T o (dP^T - c)   (dropout: P^T o (z r dP^T - c)),
+    // written over s
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key0 = j0 + 16 * kb + 4 * g;
-      f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-      if (BIAS) bv = load_bias4(brow, key0, Nk, false, rvalid);
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool masked = tile_masked || !live[qb];
+      Philox4 zw;
+      if (DROP) zw = dropout_words(dsp, row[qb], t, (uint32_t)bh, g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float arg = fmaf(s[kb][j], c2, -l2);
-        if (BIAS) arg = fmaf(bv[j], kLog2e, arg);
-        float p = fast_exp2(arg);
-        if (masked && (unsigned)(key0 + j - row_lo) >= row_span) p = 0.f;
-        const float dpz = DROP ? (dropout_keep(zw.x[kb], j, dsp.keep) ? drop_scale * dp[kb][j] : 0.f) : dp[kb][j];
-        dsv[kb][j] = p * (dpz - c_row);
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key0 = j0 + 16 * kb + 4 * g;
+        f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+        if (BIAS) bv = load_bias4(brow[qb], key0, Nk, false, rvalid[qb]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float arg = fmaf(s[kb][qb][j], c2, -l2[qb]);
+          if (BIAS) arg = fmaf(bv[j], kLog2e, arg);
+          float p = fast_exp2(arg);
+          if (masked && (unsigned)(key0 + j - row_lo[qb]) >= row_span[qb]) p = 0.f;
+          const float d = dp[kb][qb][j];
+          const float dpz = DROP ? (dropout_keep(zw.x[kb], j, dsp.keep) ? drop_scale * d : 0.f) : d;
+          s[kb][qb][j] = p * (dpz - c_row[qb]);
+        }
       }
     }
     // dQ^T += K^T D^T over the tile's two 32-key steps
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
-      const bf16x8 bop = pack_b(dsv[2 * kt2], dsv[2 * kt2 + 1]);
+      const bf16x8 bop0 = pack_b(s[2 * kt2][0], s[2 * kt2 + 1][0]);
+      const bf16x8 bop1 = pack_b(s[2 * kt2][1], s[2 * kt2 + 1][1]);
 #pragma unroll
-      for (int db = 0; db < DK / 16; ++db)
-        acc[db] = mfma(tr_read(kt + ka.tr[db] + 32 * kt2 * Tile<DK>::ROW, 16 * Tile<DK>::ROW), bop, acc[db]);
+      for (int db = 0; db < DK / 16; ++db) {
+        const bf16x8 a = tr_read(kt + ka.tr[db] + 32 * kt2 * Tile<DK>::ROW, 16 * Tile<DK>::ROW);
+        acc[0][db] = mfma(a, bop0, acc[0][db]);
+        acc[1][db] = mfma(a, bop1, acc[1][db]);
+      }
     }
   }
 
-  if (rvalid) {
-    uint16_t* out = dq + (bh * Nq + row) * (size_t)DK;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!rvalid[qb]) continue;
+    uint16_t* out = dq + (bh * Nq + row[qb]) * (size_t)DK;
 #pragma unroll
     for (int d = 0; d < DK / 16; ++d) {
       u32x2 w;
-      w[0] = cvt_pk_bf16(acc[d][0] * scale, acc[d][1] * scale);
-      w[1] = cvt_pk_bf16(acc[d][2] * scale, acc[d][3] * scale);
+      w[0] = cvt_pk_bf16(acc[qb][d][0] * scale, acc[qb][d][1] * scale);
+      w[1] = cvt_pk_bf16(acc[qb][d][2] * scale, acc[qb][d][3] * scale);
       *reinterpret_cast<u32x2*>(out + 16 * d + 4 * g) = w;
     }
   }
@@ -420,7 +459,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   // dQ first: it stores c for the dK/dV kernel
   if ((long long)a.B * a.H * a.Nq > 0)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kTile - 1) / kTile) * bh),
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kDqRows - 1) / kDqRows) * bh),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len,
                        (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
