@@ -270,11 +270,14 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
  *              written in full (keys no row can see get zero)
  *   workspace: device buffer of at least fa_bwd_workspace_bytes(B, H, Nq)
  *              bytes, 16-byte aligned; contents on entry are ignored.
- *   1 <= dk, dv <= 128; B * H <= 65535.  Rows whose lse is -inf (no allowed
+ *   1 <= dk, dv <= 128; B * H <= 65535 and ceil(max(Nq, Nk) / 64) * B * H
+ *   < 2^31 (FA_ERR_SHAPE otherwise).  Rows whose lse is -inf (no allowed
  *   key) contribute nothing.  Launches (all on `stream`, no atomics, results
- *   bitwise reproducible): c per row, then dK/dV per key tile, then dQ per
- *   query tile.  Inputs must be finite; lse must be the forward's (a
- *   different lse rescales the rebuilt probabilities).
+ *   bitwise reproducible): bf16 with head dims 64/128 -- dQ per query tile
+ *   (it also forms c = dO.O per row into the workspace), then dK/dV per key
+ *   tile; otherwise c per row, then dK/dV, then dQ.  Inputs must be finite;
+ *   lse must be the forward's (a different lse rescales the rebuilt
+ *   probabilities).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, const float* bias,

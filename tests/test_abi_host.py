@@ -157,6 +157,9 @@ def check_bwd_ex(align=fa.FA_ALIGN_BOTTOM_RIGHT, wl=-1, wr=-1, keep=256, **kw):
     ({}, OK), ({"align": fa.FA_ALIGN_TOP_LEFT, "wl": 3}, OK), ({"keep": 100}, OK), ({"keep": 0}, UNSUP),
     ({"keep": 300}, UNSUP), ({"align": 7}, UNSUP), ({"wr": -2}, UNSUP), ({"q": None}, NULL), ({"causal": 5}, UNSUP),
     ({"d_k": 200}, UNSUP),
+    ({"B": 65535, "H": 1, "Nq": 1 << 20, "Nk": 64}, OK),
+    ({"B": 65535, "H": 1, "Nq": 1 << 22, "Nk": 64}, SHAPE),  # 1-D tile grid would exceed 2^31
+    ({"B": 256, "H": 257, "Nq": 64, "Nk": 64}, SHAPE),       # B*H above the 2-D grid limit
 ])
 def test_check_bwd_ex(kw, want):
     assert check_bwd_ex(**kw) == want
