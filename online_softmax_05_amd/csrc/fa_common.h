@@ -53,13 +53,15 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Work-group -> (batch*head, query tile) mapping.
+// Work-group -> (batch*head, tile) mapping: query tiles in the forward and
+// dQ kernels, key tiles in the dK/dV kernel.
 //
 // Work-groups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
 // its own L2.  Renumbering so that XCD x works through a contiguous range of
-// logical tiles keeps the query tiles of one (batch, head) -- which re-read
-// the same K/V -- on one L2.  Inside a (batch, head) the tiles are issued
-// heaviest first when a causal mask makes later query tiles longer.
+// logical tiles keeps the tiles of one (batch, head) -- which re-read the same
+// K/V (or Q/dO) -- on one L2.  With heavy_first the tiles of a (batch, head)
+// are issued in descending order, heaviest first when a causal mask makes
+// later query tiles longer.
 struct TileCoord {
   int bh;
   int qt;
@@ -72,19 +74,6 @@ __device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool
   int r = lid - c.bh * n_qt;
   c.qt = heavy_first ? (n_qt - 1 - r) : r;
   return c;
-}
-
-// Number of keys a row block must visit: keys at or past `n_end` are masked
-// for every row of the block, so whole tiles past it are skipped ([GS]
-// section 6: entirely masked tiles can be skipped).  `last_row` is the last
-// query row of the block (global index).
-__device__ __forceinline__ int visible_key_end(int klen_eff, bool causal, int last_row, int nq, int nk) {
-  int end = klen_eff;
-  if (causal) {
-    long long c = (long long)last_row + nk - nq + 1;  // bottom-right diagonal
-    if (c < end) end = (int)(c < 0 ? 0 : c);
-  }
-  return end;
 }
 
 // Four consecutive fp32 bias values of one row starting at key0, zero past
