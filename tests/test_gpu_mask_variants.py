@@ -147,3 +147,23 @@ def test_full_size_sliding_window(dev):
     l_g = np.array([float(lse[b, h, i]) for b, h, i in rows])
     compare(torch.from_numpy(o_g), torch.from_numpy(l_g), o_ref, lse_ref, torch.bfloat16,
             "full-size window 1024 sampled rows")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_huge_windows_are_no_mask(dev, dt):
+    """Window widths near 2^31 (the row-range arithmetic is 64-bit) select
+    every key: the result equals the unwindowed call bit for bit, for both
+    alignments and with and without causal."""
+    import online_softmax_05_amd as fa
+
+    big = 2**31 - 1
+    inp = workloads.seeded_case(4300, 2, 2, 190, 270, 128, 128, DT[dt], causal=False, bias=True, k_len="random")
+    d = workloads.to_device(inp, dev)
+    for causal in (False, True):
+        for align in ("bottom_right", "top_left"):
+            say(f"huge windows {dt} causal={causal} {align}")
+            kw = dict(bias=d["bias"], k_len=d["k_len"], scale=inp["scale"], causal=causal, align=align)
+            a = fa.fa_fwd_ex(d["q"], d["k"], d["v"], **kw)
+            b = fa.fa_fwd_ex(d["q"], d["k"], d["v"], window_left=big, window_right=big, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (causal, align)
