@@ -15,8 +15,10 @@
 //   registers for the whole key loop ([OA] "Keeping Q While Processing the
 //   First K/V Tile").
 // * Key tiles of 64 keys.  K and V tiles go from global memory straight into
-//   LDS (global_load_lds_dwordx4: no staging registers, no LDS store
-//   instructions), row-major, with the 16-byte chunk c of row r stored at
+//   LDS (buffer_load_dwordx4 ... lds: no staging registers, no LDS store
+//   instructions, a fixed per-lane offset and one uniform offset per tile,
+//   the buffer's range check covering the last tile), row-major, with the
+//   16-byte chunk c of row r stored at
 //   chunk index c ^ f(r), with f chosen (by measuring LDS bank-conflict
 //   cycles) so that both operand reads below run conflict-free.  Every
 //   operand address is then a per-lane base (one per k-step for K, one per
@@ -90,7 +92,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef const __attribute__((address_space(1))) void gbl_void;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -147,7 +148,7 @@ template <int DK, int DV>
 struct LaneAddr {
   int k[DK / 32];             // K fragment base per k-step
   int v[DV / 16];             // V^T transposed-read base per 16-dim block
-  int kld[SwzTile<DK>::IPW];  // element offset (row * DK + chunk * 8) of each direct K load
+  int kld[SwzTile<DK>::IPW];  // byte offset in the tile (2 (row DK + 8 chunk)) of each direct K load
   int vld[SwzTile<DV>::IPW];
 
   __device__ __forceinline__ void init(int lane, int wave) {
@@ -164,37 +165,37 @@ struct LaneAddr {
     for (int i = 0; i < SwzTile<DK>::IPW; ++i) {
       const int slot = (wave * SwzTile<DK>::IPW + i) * 64 + lane;
       const int row = slot / SwzTile<DK>::R;
-      kld[i] = row * DK + ((slot % SwzTile<DK>::R) ^ swz<DK>(row)) * 8;
+      kld[i] = 2 * (row * DK + ((slot % SwzTile<DK>::R) ^ swz<DK>(row)) * 8);
     }
 #pragma unroll
     for (int i = 0; i < SwzTile<DV>::IPW; ++i) {
       const int slot = (wave * SwzTile<DV>::IPW + i) * 64 + lane;
       const int row = slot / SwzTile<DV>::R;
-      vld[i] = row * DV + ((slot % SwzTile<DV>::R) ^ swz<DV>(row)) * 8;
+      vld[i] = 2 * (row * DV + ((slot % SwzTile<DV>::R) ^ swz<DV>(row)) * 8);
     }
   }
 };
 
-// Direct-to-LDS loads of this wave's share of one tile whose first key row
-// is `tile` (rows_left keys remain in the tensor from there).  Rows past the
-// last key re-read the last key row (finite values whose probabilities are
-// zero), so no lane reads out of bounds.
+// One head's K (or V) as a buffer resource: base address and byte size, so
+// that the hardware range check of a buffer load covers it.
+struct HeadBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ HeadBuf head_buf(const uint16_t* base, uint32_t bytes) {
+  return HeadBuf{__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000)};
+}
+
+// Direct-to-LDS loads (buffer_load_dwordx4 ... lds) of this wave's share of
+// the tile whose first key row is row0: a uniform byte offset plus each
+// lane's fixed offset in the tile, no per-load address arithmetic.  Lanes
+// past the end of the head fail the range check and write zeros: those keys
+// are masked (p = 0), and zero V rows add nothing.
 template <int D, int IPW>
-__device__ __forceinline__ void load_tile(const uint16_t* tile, int rows_left, const int (&ld)[IPW], lds_char* dst,
-                                          int wave) {
-  if (rows_left >= kBN) {
+__device__ __forceinline__ void load_tile(const HeadBuf& b, int row0, const int* ld, lds_char* dst, int wave) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(tile + ld[i]), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0,
-                                       0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int row = ld[i] / D;
-      const int off = ld[i] + (min(row, rows_left - 1) - row) * D;
-      __builtin_amdgcn_global_load_lds((gbl_void*)(tile + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, 0);
-    }
-  }
+  for (int i = 0; i < IPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)(dst + (wave * IPW + i) * 1024), 16, ld[i], row0 * D * 2,
+                                             0, 0);
 }
 
 template <int DK>
@@ -358,8 +359,7 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
 template <int DK, int DV, bool BIAS, bool DROP>
 struct FwdTile {
   // inputs of this work-group
-  const uint16_t* kbh;
-  const uint16_t* vbh;
+  HeadBuf kbuf, vbuf;  // this head's K and V
   int nk, n_tiles;  // n_tiles: one past the last tile the work-group visits
   float c;
   int qrow0;    // global index of this lane's row in query block 0 (block 1: +16)
@@ -384,8 +384,8 @@ struct FwdTile {
                                        lds_char* knext, lds_char* vnext) {
     const int n0 = t * kBN;
     if (t + 1 < n_tiles) {
-      load_tile<DK>(kbh + (size_t)(n0 + kBN) * DK, nk - (n0 + kBN), la.kld, knext, wave);
-      load_tile<DV>(vbh + (size_t)(n0 + kBN) * DV, nk - (n0 + kBN), la.vld, vnext, wave);
+      load_tile<DK, SwzTile<DK>::IPW>(kbuf, n0 + kBN, la.kld, knext, wave);
+      load_tile<DV, SwzTile<DV>::IPW>(vbuf, n0 + kBN, la.vld, vnext, wave);
     }
     f32x4 s[4][2];
     qk_tile<DK, DV>(s, qf, kcur, la);
@@ -459,8 +459,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   FwdTile<DK, DV, BIAS, DROP> ft;
   ft.dsp = dsp;
   ft.bh = (uint32_t)tc.bh;
-  ft.kbh = k + bh * Nk * DK;
-  ft.vbh = v + bh * Nk * DV;
+  ft.kbuf = head_buf(k + bh * Nk * DK, (uint32_t)Nk * DK * 2);
+  ft.vbuf = head_buf(v + bh * Nk * DV, (uint32_t)Nk * DV * 2);
   ft.nk = Nk;
   ft.vec_bias = vec_bias;
   ft.g = g;
@@ -512,8 +512,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   ft.st.l[0] = ft.st.l[1] = 0.f;
 
   if (t_begin < t_end) {
-    load_tile<DK>(ft.kbh + (size_t)t_begin * kBN * DK, Nk - t_begin * kBN, ft.la.kld, K0, wave);
-    load_tile<DV>(ft.vbh + (size_t)t_begin * kBN * DV, Nk - t_begin * kBN, ft.la.vld, V0, wave);
+    load_tile<DK, SwzTile<DK>::IPW>(ft.kbuf, t_begin * kBN, ft.la.kld, K0, wave);
+    load_tile<DV, SwzTile<DV>::IPW>(ft.vbuf, t_begin * kBN, ft.la.vld, V0, wave);
     wait_loads();
     __syncthreads();
 
@@ -595,7 +595,9 @@ hipError_t launch_b(const FwdArgs& a, hipStream_t s) {
 
 bool fwd_bf16_fast_eligible(const FwdArgs& a) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-  return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && a.Nk > 0 && aligned(a.q) &&
+  // buffer loads address a head's K and V with 32-bit byte offsets
+  const bool fits = (long long)a.Nk * (a.dk > a.dv ? a.dk : a.dv) * 2 <= 0x7fffffffLL;
+  return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && a.Nk > 0 && fits && aligned(a.q) &&
          aligned(a.k) && aligned(a.v) && aligned(a.o) && a.block_n == kBN;
 }
 
