@@ -60,6 +60,8 @@ namespace {
 
 constexpr int kThreads = 64 * tiles::kWaves;
 
+using tiles::HeadBuf;
+using tiles::head_buf;
 using tiles::kTile;
 using tiles::kWaves;
 using tiles::Tile;
@@ -109,11 +111,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     float* __restrict__ cvec,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dq, int H, int Nq,
     int Nk, float scale, KeyRange mr, DropoutSpec dsp, float drop_scale) {
-  // one array, buffers addressed by offset (a runtime-indexed table of
-  // separate __shared__ arrays would go through a global constant table)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
-  lds_char* const kbase = (lds_char*)smem;
-  lds_char* const vbase = kbase + 2 * Tile<DK>::BYTES;
+  // separate arrays per buffer, each selected at compile time (the loop
+  // below is unrolled by two), so the compiler sees that a tile load in
+  // flight never writes the buffer being read and adds no wait for it
+  __shared__ __attribute__((aligned(1024))) char kb0[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[Tile<DV>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[Tile<DV>::BYTES];
+  lds_char* const K0 = (lds_char*)kb0;
+  lds_char* const K1 = (lds_char*)kb1;
+  lds_char* const V0 = (lds_char*)vb0;
+  lds_char* const V1 = (lds_char*)vb1;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,8 +136,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   TileAddr<DV> va;
   ka.init(lane, wave);
   va.init(lane, wave);
-  const uint16_t* kbh = k + bh * Nk * DK;
-  const uint16_t* vbh = v + bh * Nk * DV;
+  const HeadBuf kh = head_buf(k + bh * Nk * DK, (uint32_t)Nk * DK * 2);
+  const HeadBuf vh = head_buf(v + bh * Nk * DV, (uint32_t)Nk * DV * 2);
   const float c2 = scale * kLog2e;
 
   // Each wave holds 32 query rows as two 16-row blocks qb: every K or V
@@ -189,23 +197,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int t_full = (key_lo(mr, last_row) + kTile - 1) / kTile;
   const int t_full_end = key_end(mr, q0, klen) / kTile;
 
-  if (t_begin < t_end) {
-    load_tile<DK>(kbh + (size_t)t_begin * kTile * DK, Nk - t_begin * kTile, ka, kbase, wave);
-    load_tile<DV>(vbh + (size_t)t_begin * kTile * DV, Nk - t_begin * kTile, va, vbase, wave);
-  }
-  for (int t = t_begin; t < t_end; ++t) {
-    const int par = (t - t_begin) & 1;
+  // key tile t (in kt, vt) while tile t + 1 loads into kn, vn
+  auto tile = [&](int t, const lds_char* kt, const lds_char* vt, lds_char* kn, lds_char* vn) {
     wait_loads();
     __syncthreads();  // tile t visible; tile t-1's buffers free
     const int j0 = t * kTile;
     if (t + 1 < t_end) {
-      load_tile<DK>(kbh + (size_t)(j0 + kTile) * DK, Nk - (j0 + kTile), ka, kbase + (par ^ 1) * Tile<DK>::BYTES,
-                    wave);
-      load_tile<DV>(vbh + (size_t)(j0 + kTile) * DV, Nk - (j0 + kTile), va, vbase + (par ^ 1) * Tile<DV>::BYTES,
-                    wave);
+      load_tile<DK>(kh, j0 + kTile, ka.ld, kn, wave);
+      load_tile<DV>(vh, j0 + kTile, va.ld, vn, wave);
     }
-    const lds_char* kt = kbase + par * Tile<DK>::BYTES;
-    const lds_char* vt = vbase + par * Tile<DV>::BYTES;
     const bool tile_masked = t < t_full || t >= t_full_end || BIAS;
     // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of row[qb]
     f32x4 s[4][2], dp[4][2];
@@ -262,6 +262,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
         acc[1][db] = mfma(a, bop1, acc[1][db]);
       }
     }
+  };
+  if (t_begin < t_end) {
+    load_tile<DK>(kh, t_begin * kTile, ka.ld, K0, wave);
+    load_tile<DV>(vh, t_begin * kTile, va.ld, V0, wave);
+  }
+  for (int t = t_begin; t < t_end; t += 2) {
+    tile(t, K0, V0, K1, V1);
+    if (t + 1 < t_end) tile(t + 1, K1, V1, K0, V0);
   }
 
 #pragma unroll
@@ -289,7 +297,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int H, int Nq, int Nk, float scale, KeyRange mr, DropoutSpec dsp,
     float drop_scale) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Tile<DK>::BYTES + 2 * Tile<DV>::BYTES];
+  // Q and G (= dO) tiles, double buffered in separate arrays selected at
+  // compile time (the loop below is unrolled by two)
+  __shared__ __attribute__((aligned(1024))) char qb0[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb1[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char gb0[Tile<DV>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char gb1[Tile<DV>::BYTES];
   __shared__ float lbuf[2][kTile];      // L_i log2 e (0 for rows without a key)
   __shared__ float cbuf[2][kTile];      // c_i
   __shared__ int lobuf[2][kTile];       // per row: first visible key
@@ -298,8 +311,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   // [rr * kZRow + 4 g' + w] (kZRow = 17: odd stride, few bank conflicts)
   constexpr int kZRow = 17;
   __shared__ uint32_t zbuf[DROP ? 2 : 1][DROP ? kTile * kZRow : 1];
-  lds_char* const qbase = (lds_char*)smem;
-  lds_char* const gbase = qbase + 2 * Tile<DK>::BYTES;
+  lds_char* const Q0 = (lds_char*)qb0;
+  lds_char* const Q1 = (lds_char*)qb1;
+  lds_char* const G0 = (lds_char*)gb0;
+  lds_char* const G1 = (lds_char*)gb1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -317,8 +332,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   TileAddr<DV> ga;
   qa.init(lane, wave);
   ga.init(lane, wave);
-  const uint16_t* qbh = q + bh * Nq * DK;
-  const uint16_t* gbh = dout + bh * Nq * DV;
+  const HeadBuf qh = head_buf(q + bh * Nq * DK, (uint32_t)Nq * DK * 2);
+  const HeadBuf gh = head_buf(dout + bh * Nq * DV, (uint32_t)Nq * DV * 2);
 
   bf16x8 kf[DK / 32], vf[DV / 32];
   load_rows_b<DK>(kf, k + bh * Nk * DK, key, kvalid, g);
@@ -340,47 +355,55 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   const int t_end = r_hi > r_lo ? (r_hi + kTile - 1) / kTile : t0;
   const int n_tiles = max(t_end - t0, 0);
 
-  auto stage_rows = [&](int qt, int buf) {
+  // Per-row values of query tile qt, staged in LDS by threads 0..63: the
+  // loads (fetch_rows) are issued before the tile loads, and the LDS writes
+  // (store_rows) come after the products, so that waiting for these few
+  // values never waits for the tiles in flight.
+  struct Rows {
+    float l, c;
+  };
+  auto fetch_rows = [&](int qt) {
+    Rows w{kNegInf, 0.f};
+    const int r = qt * kTile + tid;
+    if (tid < kTile && r < Nq) {
+      w.l = lse[bh * Nq + r];
+      w.c = cvec[bh * Nq + r];
+    }
+    return w;
+  };
+  auto store_rows = [&](const Rows& w, int qt, int buf) {
     if (tid < kTile) {
       const int r = qt * kTile + tid;
-      const bool ok = r < Nq;
-      const float l = ok ? lse[bh * Nq + r] : kNegInf;
-      const bool live = l != kNegInf;
-      lbuf[buf][tid] = live ? l * kLog2e : 0.f;
-      cbuf[buf][tid] = ok ? cvec[bh * Nq + r] : 0.f;
+      const bool live = w.l != kNegInf;
+      lbuf[buf][tid] = live ? w.l * kLog2e : 0.f;
+      cbuf[buf][tid] = w.c;
       const int lo = key_lo(mr, r), end = live ? key_end(mr, r, klen) : 0;
       lobuf[buf][tid] = lo;
       spbuf[buf][tid] = end > lo ? (unsigned)(end - lo) : 0u;
     }
     if (DROP) {
       // one generator call per thread: row tid / 4 of the tile, group tid % 4
-      const Philox4 w = dropout_words(dsp, qt * kTile + (tid >> 2), j0 / kTile, (uint32_t)bh, tid & 3);
+      const Philox4 zw = dropout_words(dsp, qt * kTile + (tid >> 2), j0 / kTile, (uint32_t)bh, tid & 3);
       uint32_t* z = &zbuf[buf][(tid >> 2) * kZRow + 4 * (tid & 3)];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = w.x[e];
+      for (int e = 0; e < 4; ++e) z[e] = zw.x[e];
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile<DK>(qbh + (size_t)t0 * kTile * DK, Nq - t0 * kTile, qa, qbase, wave);
-    load_tile<DV>(gbh + (size_t)t0 * kTile * DV, Nq - t0 * kTile, ga, gbase, wave);
-    stage_rows(t0, 0);
-  }
-  for (int it = 0; it < n_tiles; ++it) {
+  // query tile it (in qt_l, gt_l, row values in buffer par) while tile
+  // it + 1 loads into qn, gn
+  auto tile = [&](int it, const lds_char* qt_l, const lds_char* gt_l, lds_char* qn, lds_char* gn, int par) {
     const int qt = t0 + it;
-    const int par = it & 1;
     wait_loads();
-    __syncthreads();
+    __syncthreads();  // tile it and its row values visible; tile it-1's buffers free
     const int q0 = qt * kTile;
-    if (it + 1 < n_tiles) {
-      load_tile<DK>(qbh + (size_t)(q0 + kTile) * DK, Nq - (q0 + kTile), qa, qbase + (par ^ 1) * Tile<DK>::BYTES,
-                    wave);
-      load_tile<DV>(gbh + (size_t)(q0 + kTile) * DV, Nq - (q0 + kTile), ga, gbase + (par ^ 1) * Tile<DV>::BYTES,
-                    wave);
-      stage_rows(qt + 1, par ^ 1);
+    const bool more = it + 1 < n_tiles;
+    Rows nxt{kNegInf, 0.f};
+    if (more) {
+      nxt = fetch_rows(qt + 1);
+      load_tile<DK>(qh, q0 + kTile, qa.ld, qn, wave);
+      load_tile<DV>(gh, q0 + kTile, ga.ld, gn, wave);
     }
-    const lds_char* qt_l = qbase + par * Tile<DK>::BYTES;
-    const lds_char* gt_l = gbase + par * Tile<DV>::BYTES;
     // no mask when every row of the tile exists and sees every key of the group
     const bool masked = BIAS || q0 + kTile > Nq || key_last < j0 + kTile - 1 || key_lo(mr, q0 + kTile - 1) > j0 ||
                         key_end(mr, q0, klen) < j0 + kTile;
@@ -429,6 +452,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
       for (int db = 0; db < DK / 16; ++db)
         acc_k[db] = mfma(tr_read(qt_l + qa.tr[db] + 32 * k2 * Tile<DK>::ROW, 16 * Tile<DK>::ROW), dop, acc_k[db]);
     }
+    if (more) store_rows(nxt, qt + 1, par ^ 1);
+  };
+  if (n_tiles > 0) {
+    load_tile<DK>(qh, t0 * kTile, qa.ld, Q0, wave);
+    load_tile<DV>(gh, t0 * kTile, ga.ld, G0, wave);
+    store_rows(fetch_rows(t0), t0, 0);
+  }
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile(it, Q0, G0, Q1, G1, 0);
+    if (it + 1 < n_tiles) tile(it + 1, Q1, G1, Q0, G0, 1);
   }
 
   if (kvalid) {
@@ -482,8 +515,11 @@ hipError_t launch_b(const BwdArgs& a, hipStream_t s) {
 
 bool bwd_bf16_mfma_eligible(const BwdArgs& a) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  // tiles are read with buffer loads: a head's Q, dO, K and V bytes must fit 31 bits
+  const int dmax = a.dk > a.dv ? a.dk : a.dv;
   return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && aligned(a.q) && aligned(a.k) &&
-         aligned(a.v) && aligned(a.dout) && aligned(a.dq_out) && aligned(a.dk_out) && aligned(a.dv_out);
+         aligned(a.v) && aligned(a.dout) && aligned(a.dq_out) && aligned(a.dk_out) && aligned(a.dv_out) &&
+         tiles::head_fits(a.Nq, dmax) && tiles::head_fits(a.Nk, dmax);
 }
 
 hipError_t launch_bwd_bf16_mfma(const BwdArgs& a, hipStream_t s) {

@@ -40,6 +40,8 @@ namespace {
 
 using tiles::cvt_pk_bf16;
 using tiles::frag_read;
+using tiles::HeadBuf;
+using tiles::head_buf;
 using tiles::kTile;
 using tiles::kWaves;
 using tiles::lds_char;
@@ -177,11 +179,19 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
     const int32_t* __restrict__ k_len, float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int BH, int Nq,
     int Nk, int chunk, int max_chunks, float scale_log2, int causal) {
   constexpr int ROW = Tile<kD>::ROW;
-  // K and V tiles, double buffered; reused for the end-of-chunk merge
-  __shared__ __attribute__((aligned(1024))) char smem[4 * Tile<kD>::BYTES];
+  // K and V tiles, double buffered in separate arrays selected at compile
+  // time (the loop below is unrolled by two); K0 and V0 hold the
+  // end-of-chunk merge afterwards
+  __shared__ __attribute__((aligned(1024))) char kb0[Tile<kD>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[Tile<kD>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[Tile<kD>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[Tile<kD>::BYTES];
   __shared__ float red_ml[kWaves][kMaxRows][2];
-  lds_char* const kbase = (lds_char*)smem;
-  lds_char* const vbase = kbase + 2 * Tile<kD>::BYTES;
+  lds_char* const K0 = (lds_char*)kb0;
+  lds_char* const K1 = (lds_char*)kb1;
+  lds_char* const V0 = (lds_char*)vb0;
+  lds_char* const V1 = (lds_char*)vb1;
+  static_assert(2 * kMaxRows * kD * 4 <= Tile<kD>::BYTES, "two waves' merge rows fit one tile buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,29 +216,23 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
 
   TileAddr<kD> ta;
   ta.init(lane, wave);
-  const uint16_t* kbh = k + bh * Nk * kD;
-  const uint16_t* vbh = v + bh * Nk * kD;
+  const HeadBuf kh = head_buf(k + bh * Nk * kD, (uint32_t)Nk * kD * 2);
+  const HeadBuf vh = head_buf(v + bh * Nk * kD, (uint32_t)Nk * kD * 2);
 
   float m = kNegInf, l = 0.f;  // this wave's state for row r16 (l: this lane's share)
   f32x4 o[kD / 16];            // O^T: dims 16db + 4g + j of row r16
 #pragma unroll
   for (int d = 0; d < kD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile<kD, tiles::kNonTemporal>(kbh + (size_t)c0 * kD, Nk - c0, ta, kbase, wave);
-  load_tile<kD, tiles::kNonTemporal>(vbh + (size_t)c0 * kD, Nk - c0, ta, vbase, wave);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int par = t & 1;
+  // key tile t (in kt, vt) while tile t + 1 loads into kn, vn
+  auto tile = [&](int t, const lds_char* kt, const lds_char* vt, lds_char* kn, lds_char* vn) {
     wait_loads();
     __syncthreads();
     const int j0 = c0 + t * kTile;
     if (t + 1 < n_tiles) {
-      load_tile<kD, tiles::kNonTemporal>(kbh + (size_t)(j0 + kTile) * kD, Nk - (j0 + kTile), ta, kbase + (par ^ 1) * Tile<kD>::BYTES,
-                    wave);
-      load_tile<kD, tiles::kNonTemporal>(vbh + (size_t)(j0 + kTile) * kD, Nk - (j0 + kTile), ta, vbase + (par ^ 1) * Tile<kD>::BYTES,
-                    wave);
+      load_tile<kD, tiles::kNonTemporal>(kh, j0 + kTile, ta.ld, kn, wave);
+      load_tile<kD, tiles::kNonTemporal>(vh, j0 + kTile, ta.ld, vn, wave);
     }
-    const lds_char* kt = kbase + par * Tile<kD>::BYTES;
-    const lds_char* vt = vbase + par * Tile<kD>::BYTES;
     // S^T for this wave's 16 keys: a lane holds keys 16 wave + 4g + j of row r16
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -259,17 +263,25 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
       const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vt + ta.tr[d] + 16 * wave * ROW));
       o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[d], 0, 0, 0);
     }
+  };
+  load_tile<kD, tiles::kNonTemporal>(kh, c0, ta.ld, K0, wave);
+  load_tile<kD, tiles::kNonTemporal>(vh, c0, ta.ld, V0, wave);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(t, K0, V0, K1, V1);
+    if (t + 1 < n_tiles) tile(t + 1, K1, V1, K0, V0);
   }
 
   // merge the four waves' states per row ([GS] section 4) through LDS
   l = quad_sum(l);
   wait_loads();
   __syncthreads();  // tile buffers are free
-  lds_float* red_u = (lds_float*)smem;  // [wave][row][dim]
+  // [wave][row][dim]: waves 0 and 1 in K0, waves 2 and 3 in V0
+  const auto red_u = [&](int w) { return (lds_float*)((w < 2 ? K0 : V0) + (w & 1) * kMaxRows * kD * 4); };
+  lds_float* const mine = red_u(wave);
 #pragma unroll
   for (int d = 0; d < kD / 16; ++d)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red_u[(wave * kMaxRows + r16) * kD + 16 * d + 4 * g + j] = o[d][j];
+    for (int j = 0; j < 4; ++j) mine[r16 * kD + 16 * d + 4 * g + j] = o[d][j];
   if (g == 0) {
     red_ml[wave][r16][0] = m;
     red_ml[wave][r16][1] = l;
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float a = fast_exp2(red_ml[w][i][0] - mu);
-      u = fmaf(a, red_u[(w * kMaxRows + i) * kD + dd], u);
+      u = fmaf(a, red_u(w)[i * kD + dd], u);
       ll = fmaf(a, red_ml[w][i][1], ll);
     }
     const size_t si = state_index(bh, c, i, max_chunks, Nq);
@@ -367,7 +379,8 @@ hipError_t launch_mq(const DecodeMqArgs& a, hipStream_t stream, bool mfma) {
 
 hipError_t launch_decode_mq_bf16(const DecodeMqArgs& a, hipStream_t s) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-  const bool mfma = a.dk == kD && a.dv == kD && aligned(a.q) && aligned(a.k) && aligned(a.v);
+  const bool mfma = a.dk == kD && a.dv == kD && aligned(a.q) && aligned(a.k) && aligned(a.v) &&
+                    tiles::head_fits(a.Nk, kD);  // K/V tiles are read with buffer loads
   return launch_mq<uint16_t>(a, s, mfma);
 }
 hipError_t launch_decode_mq_f32(const DecodeMqArgs& a, hipStream_t s) { return launch_mq<float>(a, s, false); }

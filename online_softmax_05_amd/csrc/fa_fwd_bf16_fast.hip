@@ -176,14 +176,13 @@ struct LaneAddr {
   }
 };
 
-// One head's K (or V) as a buffer resource: base address and byte size, so
-// that the hardware range check of a buffer load covers it.
+// One head's K (or V): base address and byte size, turned into a buffer
+// resource at each load so that the hardware range check covers the head.
 struct HeadBuf {
-  __amdgpu_buffer_rsrc_t r;
+  const uint16_t* base;
+  uint32_t bytes;
 };
-__device__ __forceinline__ HeadBuf head_buf(const uint16_t* base, uint32_t bytes) {
-  return HeadBuf{__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000)};
-}
+__device__ __forceinline__ HeadBuf head_buf(const uint16_t* base, uint32_t bytes) { return HeadBuf{base, bytes}; }
 
 // Direct-to-LDS loads (buffer_load_dwordx4 ... lds) of this wave's share of
 // the tile whose first key row is row0: a uniform byte offset plus each
@@ -194,8 +193,9 @@ template <int D, int IPW>
 __device__ __forceinline__ void load_tile(const HeadBuf& b, int row0, const int* ld, lds_char* dst, int wave) {
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)(dst + (wave * IPW + i) * 1024), 16, ld[i], row0 * D * 2,
-                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc((void*)b.base, (short)0, (int)b.bytes, 0x00020000),
+        (lds_void*)(dst + (wave * IPW + i) * 1024), 16, ld[i], row0 * D * 2, 0, 0);
 }
 
 template <int DK>

@@ -18,7 +18,6 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) float lds_float;
-typedef const __attribute__((address_space(1))) void gbl_void;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -56,7 +55,7 @@ template <int D>
 struct TileAddr {
   int frag[D / 32];  // operand read (tile row 16blk + r16, dims 32t + 8g .. +7): + 16 blk ROW
   int tr[D / 16];    // transposed read of dim block db (tile rows 32kt + 16h + 4g + e): + (32kt + 16h) ROW
-  int ld[Tile<D>::IPW];
+  int ld[Tile<D>::IPW];  // byte offset in the tile of each of this wave's direct loads
 
   __device__ __forceinline__ void init(int lane, int wave) {
     constexpr int ROW = Tile<D>::ROW;
@@ -70,30 +69,41 @@ struct TileAddr {
     for (int i = 0; i < Tile<D>::IPW; ++i) {
       const int slot = (wave * Tile<D>::IPW + i) * 64 + lane;
       const int row = slot / Tile<D>::R;
-      ld[i] = row * D + ((slot % Tile<D>::R) ^ swz<D>(row)) * 8;
+      ld[i] = 2 * (row * D + ((slot % Tile<D>::R) ^ swz<D>(row)) * 8);
     }
   }
 };
 
-// Direct-to-LDS load of this wave's share of a tile whose first row is `src`
-// (rows_left rows remain in the tensor); rows past the end re-read the last
-// row, so no lane reads out of bounds (those rows are masked).  CPOL is the
-// load's cache policy: 0, or kNonTemporal for data read once per call.
+// One head's rows of a tensor: base address and byte size, turned into a
+// buffer resource at each load so that the hardware range check covers the
+// head.  The byte size must fit in 31 bits (the callers' eligibility checks
+// say so).
+struct HeadBuf {
+  const uint16_t* base;
+  uint32_t bytes;
+};
+__device__ __forceinline__ HeadBuf head_buf(const uint16_t* base, uint32_t bytes) { return HeadBuf{base, bytes}; }
+
+// Direct-to-LDS load (buffer_load_dwordx4 ... lds) of this wave's share of
+// the tile whose first row is row0: one uniform byte offset per tile plus
+// each lane's fixed offset (ld = TileAddr<D>::ld), no per-load address
+// arithmetic.  Lanes past the
+// end of the head fail the range check and write zeros (those rows are
+// masked; zero rows add nothing to the products).  CPOL is the cache policy:
+// 0, or kNonTemporal for data read once per call.
 constexpr int kNonTemporal = 2;
 template <int D, int CPOL = 0>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int rows_left, const TileAddr<D>& a, lds_char* dst,
-                                          int wave) {
+__device__ __forceinline__ void load_tile(const HeadBuf& b, int row0, const int* ld, lds_char* dst, int wave) {
   constexpr int IPW = Tile<D>::IPW;
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    int off = a.ld[i];
-    if (rows_left < kTile) {
-      const int row = off / D;
-      off += (min(row, rows_left - 1) - row) * D;
-    }
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + off), (lds_void*)(dst + (wave * IPW + i) * 1024), 16, 0, CPOL);
-  }
+  for (int i = 0; i < IPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc((void*)b.base, (short)0, (int)b.bytes, 0x00020000),
+        (lds_void*)(dst + (wave * IPW + i) * 1024), 16, ld[i], row0 * D * 2, 0, CPOL);
 }
+
+// Largest tensor rows * D for which a head's bytes fit the buffer range.
+__host__ __device__ constexpr bool head_fits(long long rows, int d) { return rows * d * 2 <= 0x7fffffffLL; }
 
 __device__ __forceinline__ bf16x8 frag_read(const lds_char* p) { return *(const lds_bf16x8*)p; }
 
