@@ -58,10 +58,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 //
 // Work-groups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
 // its own L2.  Renumbering so that XCD x works through a contiguous range of
-// logical tiles keeps the tiles of one (batch, head) -- which re-read the same
-// K/V (or Q/dO) -- on one L2.  With heavy_first the tiles of a (batch, head)
-// are issued in descending order, heaviest first when a causal mask makes
-// later query tiles longer.
+// logical tiles keeps the tiles of a few (batch, head) blocks -- which re-read
+// the same K/V (or Q/dO) -- on one L2.  Within the range the (batch, head)
+// blocks go in pairs, the two blocks' tiles alternating, and with heavy_first
+// each block's tiles come in descending order (heaviest first when a causal
+// mask makes later query tiles longer).  Issuing one block's tiles after the
+// other instead left the heaviest tiles of the range's last blocks starting
+// when the rest were nearly done: a list-scheduling model of the causal
+// 4x32x4096 prefill puts that tail at 10.6% of the launch, and pairs remove
+// it while fewer blocks are in flight at once (at most 4 instead of 6).
 struct TileCoord {
   int bh;
   int qt;
@@ -69,9 +74,16 @@ struct TileCoord {
 __device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool heavy_first) {
   int lid = pid;
   if ((total & 7) == 0) lid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int n_bh = total / n_qt;
+  const int pr = lid / (2 * n_qt);  // pair of blocks 2pr, 2pr + 1
+  int r = lid - pr * 2 * n_qt;
   TileCoord c;
-  c.bh = lid / n_qt;
-  int r = lid - c.bh * n_qt;
+  if (2 * pr + 1 < n_bh) {
+    c.bh = 2 * pr + (r & 1);
+    r >>= 1;
+  } else {
+    c.bh = 2 * pr;  // the last block of an odd count goes alone
+  }
   c.qt = heavy_first ? (n_qt - 1 - r) : r;
   return c;
 }
