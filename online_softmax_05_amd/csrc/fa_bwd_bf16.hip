@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, (Nq + kDqRows - 1) / kDqRows, mr.wr >= 0);
+  const int n_qt = (Nq + kDqRows - 1) / kDqRows;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, mr.wr >= 0,
+                                tile_group(mr.wl < 0 && mr.wr >= 0, (int)(gridDim.x / n_qt),
+                                           (long long)Nk * (DK + DV) * 2));
   const size_t bh = (size_t)tc.bh;
   const int b = (int)(bh / H);
   const int q0 = tc.qt * kDqRows;

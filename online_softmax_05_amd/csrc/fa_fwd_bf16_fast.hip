@@ -446,7 +446,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   // every work-group does the same work and the grid drains evenly.
   const bool pair = FA_FAST_PAIR && mr.wl < 0 && mr.wr == 0;
   const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, mr.wr >= 0 && !pair);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, mr.wr >= 0 && !pair,
+                                tile_group(mr.wl < 0 && mr.wr >= 0 && !pair, (int)(gridDim.x / n_units),
+                                           (long long)Nk * (DK + DV) * 2));
   const int n_pass = (pair && 2 * tc.qt + 1 != n_qt) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
   const int qt = pair ? (pass == 0 ? n_qt - 1 - tc.qt : tc.qt) : tc.qt;
