@@ -72,16 +72,6 @@ constexpr int kBM = 32 * kWaves;  // query rows per work-group
 constexpr int kBN = 64;           // keys per tile
 constexpr float kRebase = 8.f;    // lazy rebasing threshold (log2 units)
 
-// Causal balance: 1 = one work-group per (heavy, light) query-tile pair;
-// 0 = one work-group per query tile, heaviest tile of each (batch, head)
-// first.  Pairing halves the work-groups per head, so the 64 work-groups an
-// XCD holds at once span twice as many heads and their K/V (2 MiB per head
-// at 4096 keys) no longer fits the XCD's 4 MiB L2: measured HBM traffic rose
-// from 1.0x to 1.7x the algorithmic bytes for 3% more speed.  Off by default.
-#ifndef FA_FAST_PAIR
-#define FA_FAST_PAIR 0
-#endif
-
 // Pace LDS operand reads against the MFMAs that consume them (bounds the
 // registers held by fragments in flight).
 #ifndef FA_FAST_PACE
@@ -202,6 +192,13 @@ template <int DK>
 struct QFrag {
   bf16x8 f[2][DK / 32];  // [query block][k-step]: dims 32t + 8g .. +7
 };
+
+// 16 bytes of a head's Q at byte offset off; zeros at or past `bytes` (the
+// hardware range check), so rows past Nq need no branch.
+__device__ __forceinline__ u32x4 load_q16(const uint16_t* qbh, uint32_t bytes, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(
+      __builtin_amdgcn_make_buffer_rsrc((void*)qbh, (short)0, (int)bytes, 0x00020000), off, 0, 0);
+}
 
 // S^T (keys x queries) of one tile: s[kb][qb] is the 16x16 block of key
 // block kb and query block qb; a lane holds keys 16kb + 4g + j of query
@@ -441,20 +438,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
 
-  // Under a causal mask query tile i visits about i + 1 key tiles; a
-  // work-group takes the pair (n_qt - 1 - u, u), heavy one first, so that
-  // every work-group does the same work and the grid drains evenly.
-  const bool pair = FA_FAST_PAIR && mr.wl < 0 && mr.wr == 0;
-  const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_units, mr.wr >= 0 && !pair,
-                                tile_group(mr.wl < 0 && mr.wr >= 0 && !pair, (int)(gridDim.x / n_units),
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, mr.wr >= 0,
+                                tile_group(mr.wl < 0 && mr.wr >= 0, (int)(gridDim.x / n_qt),
                                            (long long)Nk * (DK + DV) * 2));
-  const int n_pass = (pair && 2 * tc.qt + 1 != n_qt) ? 2 : 1;
-  for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = pair ? (pass == 0 ? n_qt - 1 - tc.qt : tc.qt) : tc.qt;
+  const int qt = tc.qt;
   const int b = tc.bh / H;
   const int q0 = qt * kBM;
-  const int klen = clamp_klen(k_len, b, Nk);
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
 
@@ -468,6 +457,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   ft.g = g;
   ft.la.init(lane, wave);
 
+  // The first K/V tile and Q load together, before anything waits on
+  // memory (the key length, the mask range): the start of a work-group then
+  // costs one memory latency.  The first tile's rows begin at the first
+  // row's lowest visible key, which the key length does not move; a query
+  // tile left with no key tile ignores the loaded tile.
+  const int t_begin = key_lo(mr, q0) / kBN;
+  const bool t0_in = t_begin < (Nk + kBN - 1) / kBN;
+  if (t0_in) {
+    load_tile<DK, SwzTile<DK>::IPW>(ft.kbuf, t_begin * kBN, ft.la.kld, K0, wave);
+    load_tile<DV, SwzTile<DV>::IPW>(ft.vbuf, t_begin * kBN, ft.la.vld, V0, wave);
+  }
+  u32x4 qw[2][DK / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint32_t row = (uint32_t)(q0 + wave * 32 + qb * 16 + r16);
+#pragma unroll
+    for (int t = 0; t < DK / 32; ++t)
+      qw[qb][t] = load_q16(qbh, (uint32_t)Nq * DK * 2, (row * DK + 32 * t + 8 * g) * 2);
+  }
+
+  const int klen = clamp_klen(k_len, b, Nk);
   int qrow[2];
   ft.qrow0 = q0 + wave * 32 + r16;
   ft.klen = klen;
@@ -484,7 +494,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int last_row = min(q0 + kBM, Nq) - 1;
   const int kbeg = key_lo(mr, q0);
   const int kend = key_end(mr, last_row, klen);
-  const int t_begin = kbeg / kBN;
   const int t_end = kend > kbeg ? (kend + kBN - 1) / kBN : t_begin;
   ft.n_tiles = t_end;
 
@@ -492,19 +501,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   // the sign of Q, exactly; zero becomes a tiny positive value)
   const bool neg_scale = scale_log2 < 0.f;
   ft.c = fmaxf(fabsf(scale_log2), 1e-30f);
-  {
-    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const uint16_t* qr = qbh + (size_t)(ft.rvalid[qb] ? qrow[qb] : 0) * DK;
-#pragma unroll
-      for (int t = 0; t < DK / 32; ++t) {
-        u32x4 w = ft.rvalid[qb] ? *reinterpret_cast<const u32x4*>(qr + 32 * t + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-        w[0] ^= flip; w[1] ^= flip; w[2] ^= flip; w[3] ^= flip;
-        ft.qf.f[qb][t] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-  }
 #pragma unroll
   for (int d = 0; d < DV / 16; ++d) {
     ft.o[d][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -512,13 +508,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   }
   ft.st.m[0] = ft.st.m[1] = kNegInf;
   ft.st.l[0] = ft.st.l[1] = 0.f;
+  wait_loads();
+  __syncthreads();
+  {
+    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int t = 0; t < DK / 32; ++t) {
+        u32x4 w = qw[qb][t];
+        w[0] ^= flip; w[1] ^= flip; w[2] ^= flip; w[3] ^= flip;
+        ft.qf.f[qb][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
 
   if (t_begin < t_end) {
-    load_tile<DK, SwzTile<DK>::IPW>(ft.kbuf, t_begin * kBN, ft.la.kld, K0, wave);
-    load_tile<DV, SwzTile<DV>::IPW>(ft.vbuf, t_begin * kBN, ft.la.vld, V0, wave);
-    wait_loads();
-    __syncthreads();
-
     // Tile t sits in buffer 0 or 1 by the parity of t - t_begin.  The
     // unmasked run starts at an even distance from t_begin (a tile moved
     // into the masked run is still computed correctly), so it always starts
@@ -569,15 +574,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     if (lse != nullptr && g == 0)
       lse[bh * Nq + qrow[qb]] = nonempty ? (ft.st.m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
-  }  // pass
 }
 
 template <int DK, int DV, bool BIAS, bool DROP>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
-  const bool pair = FA_FAST_PAIR && a.wl < 0 && a.wr == 0;
-  const int n_units = pair ? (n_qt + 1) / 2 : n_qt;
-  const long long total = (long long)n_units * a.H * a.B;
+  const long long total = (long long)n_qt * a.H * a.B;
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & 15) == 0);
   hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
@@ -598,7 +600,9 @@ hipError_t launch_b(const FwdArgs& a, hipStream_t s) {
 bool fwd_bf16_fast_eligible(const FwdArgs& a) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   // buffer loads address a head's K and V with 32-bit byte offsets
-  const bool fits = (long long)a.Nk * (a.dk > a.dv ? a.dk : a.dv) * 2 <= 0x7fffffffLL;
+  // (Q too, up to the last 128-row tile)
+  const bool fits = (long long)a.Nk * (a.dk > a.dv ? a.dk : a.dv) * 2 <= 0x7fffffffLL &&
+                    ((long long)a.Nq + kBM) * a.dk * 2 <= 0x7fffffffLL;
   return (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) && a.Nk > 0 && fits && aligned(a.q) &&
          aligned(a.k) && aligned(a.v) && aligned(a.o) && a.block_n == kBN;
 }
