@@ -74,9 +74,11 @@ struct TileCoord {
   int bh;
   int qt;
 };
+__device__ __forceinline__ int xcd_renumber(int pid, int total) {
+  return (total & 7) == 0 ? (pid & 7) * (total >> 3) + (pid >> 3) : pid;
+}
 __device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool heavy_first, int group = 2) {
-  int lid = pid;
-  if ((total & 7) == 0) lid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int lid = xcd_renumber(pid, total);
   const int n_bh = total / n_qt;
   const int gi = lid / (group * n_qt);  // group of blocks group*gi .. +group-1
   int r = lid - gi * group * n_qt;
@@ -94,9 +96,24 @@ __device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool
 // 2 MiB; otherwise pairs.  Measured on the causal bf16 prefill 4x32x4096 (K
 // and V 2 MiB per head): 1.5% faster than pairs, dropout 3.7%; long context
 // 1x16x16384 with groups of 4: 30% slower.
-__device__ __forceinline__ int tile_group(bool growing, int n_bh, long long kv_bytes) {
+__host__ __device__ __forceinline__ int tile_group(bool growing, int n_bh, long long kv_bytes) {
   return (growing && n_bh >= 64 && kv_bytes <= (2ll << 20)) ? 4 : 2;
 }
+
+// Division of x < 2^31 by a launch constant d >= 1 without a divide:
+// floor(x / d) = floor(x * m / 2^s) with s = 31 + ceil(log2 d) and
+// m = ceil(2^s / d) < 2^32, exact because m*d - 2^s < d <= 2^(s - 31)
+// (the round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  return FastDiv{(uint32_t)(((1ull << (31 + l)) + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ int fast_div(int x, FastDiv d) { return (int)(((uint64_t)(uint32_t)x * d.m) >> d.s); }
 
 // Four consecutive fp32 bias values of one row starting at key0, zero past
 // nk or for an invalid row; vec: the row is 16-byte aligned and nk % 4 == 0.

@@ -93,12 +93,16 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// max / sum over the four lanes q, q+16, q+32, q+48 that share a query
+// max / sum over the four lanes q, q+16, q+32, q+48 that share a query.
+// The max is med3(a, b, FLT_MAX) (a and b are finite or -inf): fmaxf would
+// first quiet each operand that comes out of a lane swap (two more
+// instructions per max), and a +inf bound folds back into fmaxf.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.402823466e38f); }
 __device__ __forceinline__ float quad_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float quad_sum(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -418,12 +422,36 @@ struct FwdTile {
   }
 };
 
+// The grid's tile order (map_tile's grouped, heaviest-first order) with its
+// divisions by launch constants precomputed: group * n_qt and H.
+struct FwdMap {
+  FastDiv by_gq, by_h;
+  int n_qt, n_bh, group;  // group: 2 or 4 blocks
+};
+
+// x / d and x % d for d in 1..4
+__device__ __forceinline__ int div_small(int x, int d) {
+  return d == 3 ? (int)(((uint64_t)(uint32_t)x * 0xAAAAAAABull) >> 33) : x >> (d >> 1);
+}
+
+__device__ __forceinline__ TileCoord fwd_tile(int pid, int total, const FwdMap& fm, bool heavy_first) {
+  const int lid = xcd_renumber(pid, total);
+  const int gi = fast_div(lid, fm.by_gq);
+  const int r = lid - gi * fm.group * fm.n_qt;
+  const int gsz = min(fm.group, fm.n_bh - gi * fm.group);  // the last group may be smaller
+  const int qi = div_small(r, gsz);
+  TileCoord c;
+  c.bh = gi * fm.group + (r - qi * gsz);
+  c.qt = heavy_first ? (fm.n_qt - 1 - qi) : qi;
+  return c;
+}
+
 template <int DK, int DV, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ k_len, uint16_t* __restrict__ o,
     float* __restrict__ lse, int H, int Nq, int Nk, float scale_log2, KeyRange mr, DropoutSpec dsp,
-    float drop_scale, int vec_bias, int n_qt) {
+    float drop_scale, int vec_bias, FwdMap fm) {
   __shared__ __attribute__((aligned(1024))) char kbuf0[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[SwzTile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[SwzTile<DV>::BYTES];
@@ -438,11 +466,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, n_qt, mr.wr >= 0,
-                                tile_group(mr.wl < 0 && mr.wr >= 0, (int)(gridDim.x / n_qt),
-                                           (long long)Nk * (DK + DV) * 2));
+  const TileCoord tc = fwd_tile(blockIdx.x, gridDim.x, fm, mr.wr >= 0);
   const int qt = tc.qt;
-  const int b = tc.bh / H;
+  const int b = fast_div(tc.bh, fm.by_h);
   const int q0 = qt * kBM;
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
@@ -580,11 +606,17 @@ template <int DK, int DV, bool BIAS, bool DROP>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long total = (long long)n_qt * a.H * a.B;
+  FwdMap fm;
+  fm.n_qt = n_qt;
+  fm.n_bh = a.B * a.H;
+  fm.group = tile_group(a.wl < 0 && a.wr >= 0, fm.n_bh, (long long)a.Nk * (DK + DV) * 2);
+  fm.by_gq = make_fastdiv((uint32_t)(fm.group * n_qt));
+  fm.by_h = make_fastdiv((uint32_t)a.H);
   const bool vec_b = (a.Nk % 4 == 0) && (((uintptr_t)a.bias & 15) == 0);
   hipLaunchKernelGGL((fwd_bf16_fast_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.bias, a.k_len,
                      (uint16_t*)a.o, a.lse, a.H, a.Nq, a.Nk, a.scale * kLog2e, KeyRange{a.off, a.wl, a.wr},
-                     DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256}, 256.f / (float)a.keep_256, (int)vec_b, n_qt);
+                     DropoutSpec{a.seed_lo, a.seed_hi, a.keep_256}, 256.f / (float)a.keep_256, (int)vec_b, fm);
   return hipGetLastError();
 }
 

@@ -219,6 +219,31 @@ def test_seeded_sweep(dev, case):
     compare(o, lse, o_ref, lse_ref, DT[dt], f"sweep {n}")
 
 
+# (B, H, Nq, Nk, causal): grids of the fast bf16 kernel whose (batch, head)
+# count is not a multiple of 8 or of the tile group (4 for causal grids of
+# 64 or more blocks, else 2), so that the last group holds 1, 2 or 3 blocks
+FAST_GRIDS = [
+    (13, 5, 300, 300, True),   # 65 blocks, groups of 4, last group 1
+    (3, 22, 520, 520, True),   # 66 blocks, groups of 4, last group 2
+    (1, 67, 129, 129, True),   # 67 blocks, groups of 4, last group 3
+    (7, 9, 200, 333, True),    # 63 blocks, pairs, last group 1
+    (5, 13, 257, 600, False),  # 65 blocks, pairs (no causal mask), last group 1
+]
+
+
+@pytest.mark.parametrize("case", FAST_GRIDS, ids=lambda c: "x".join(map(str, c)))
+def test_fast_kernel_odd_grids(dev, case):
+    """Every (batch, head, query tile) of the fast kernel's grid is computed
+    once, whatever the grouping of its blocks."""
+    B, H, nq, nk, causal = case
+    inp = workloads.seeded_case(7000 + B * H + nq, B, H, nq, nk, 128, 128, torch.bfloat16, causal=causal,
+                                k_len="random")
+    say(f"fast kernel grid {case}")
+    o, lse = run_fwd(inp, dev)
+    o_ref, lse_ref = oracle_full(inp)
+    compare(o, lse, o_ref, lse_ref, torch.bfloat16, f"fast grid {case}")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-3, 3.0])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_scale_values(dev, scale, dt):
