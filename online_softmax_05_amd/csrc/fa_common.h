@@ -69,7 +69,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // it while fewer blocks are in flight at once (at most 4 instead of 6).
 // Groups of 4 blocks balance the measured launch further where a block's K/V
 // is small and many blocks share an XCD (tile_group); where a block's K/V is
-// large (long sequences) groups of 4 thrash the L2 and pairs stay.
+// large (long sequences) grouping only multiplies the HBM reads and blocks
+// go one at a time.
 struct TileCoord {
   int bh;
   int qt;
@@ -93,11 +94,15 @@ __device__ __forceinline__ TileCoord map_tile(int pid, int total, int n_qt, bool
 // Group size for map_tile: 4 blocks when tile work grows along the tile
 // axis (growing: a causal mask without a left window), at least 64 blocks
 // share the launch (8 or more per XCD) and a block's K and V take at most
-// 2 MiB; otherwise pairs.  Measured on the causal bf16 prefill 4x32x4096 (K
-// and V 2 MiB per head): 1.5% faster than pairs, dropout 3.7%; long context
-// 1x16x16384 with groups of 4: 30% slower.
+// 2 MiB; pairs for other blocks of at most 2 MiB; one block at a time above
+// that.  Measured on the causal bf16 prefill 4x32x4096 (K and V 2 MiB per
+// head): groups of 4 1.5% faster than pairs, dropout 3.7%.  Long context
+// 1x16x16384 (8 MiB per head): groups of 4 30% slower than pairs, and pairs
+// as fast as one block at a time but with twice the HBM reads (each block's
+// K/V swept by half as many tiles at once).
 __host__ __device__ __forceinline__ int tile_group(bool growing, int n_bh, long long kv_bytes) {
-  return (growing && n_bh >= 64 && kv_bytes <= (2ll << 20)) ? 4 : 2;
+  if (kv_bytes > (2ll << 20)) return 1;
+  return (growing && n_bh >= 64) ? 4 : 2;
 }
 
 // Division of x < 2^31 by a launch constant d >= 1 without a divide:

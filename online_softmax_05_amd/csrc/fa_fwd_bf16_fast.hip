@@ -426,7 +426,7 @@ struct FwdTile {
 // divisions by launch constants precomputed: group * n_qt and H.
 struct FwdMap {
   FastDiv by_gq, by_h;
-  int n_qt, n_bh, group;  // group: 2 or 4 blocks
+  int n_qt, n_bh, group;  // group: 1, 2 or 4 blocks
 };
 
 // x / d and x % d for d in 1..4

@@ -221,8 +221,10 @@ def test_seeded_sweep(dev, case):
 
 # (B, H, Nq, Nk, causal): grids of the fast bf16 kernel whose (batch, head)
 # count is not a multiple of 8 or of the tile group (4 for causal grids of
-# 64 or more blocks, else 2), so that the last group holds 1, 2 or 3 blocks
+# 64 or more blocks, else 2; 1 above 2 MiB of K/V per block), so that the
+# last group holds 1, 2 or 3 blocks
 FAST_GRIDS = [
+    (1, 3, 600, 4200, True),   # 3 blocks of 2.05 MiB K/V: one block at a time
     (13, 5, 300, 300, True),   # 65 blocks, groups of 4, last group 1
     (3, 22, 520, 520, True),   # 66 blocks, groups of 4, last group 2
     (1, 67, 129, 129, True),   # 67 blocks, groups of 4, last group 3
