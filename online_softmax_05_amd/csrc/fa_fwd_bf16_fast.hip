@@ -376,6 +376,7 @@ struct FwdTile {
   QFrag<DK> qf;
   f32x4 o[DV / 16][2];
   RowState st;
+  int wfirst, wlast;  // this wave's first and last query row (wlast < wfirst: none)
 
   // One tile t (K_t and V_t in kcur / vcur) while tile t+1 loads into
   // knext / vnext: S^T, softmax, rescale, O += P V, then the barrier that
@@ -387,6 +388,18 @@ struct FwdTile {
     if (t + 1 < n_tiles) {
       load_tile<DK, SwzTile<DK>::IPW>(kbuf, n0 + kBN, la.kld, knext, wave);
       load_tile<DV, SwzTile<DV>::IPW>(vbuf, n0 + kBN, la.vld, vnext, wave);
+    }
+    // A masked tile that none of this wave's rows can see changes nothing
+    // (all its P are zero, the reference stays): skip its products.  The
+    // row ranges only grow with the row, so the first row's lowest key and
+    // the last row's end bound them all.
+    if (MASK) {
+      const bool dead = wlast < wfirst || key_end(mr, wlast, klen) <= n0 || key_lo(mr, wfirst) >= n0 + kBN;
+      if (__builtin_amdgcn_readfirstlane((int)dead)) {
+        wait_loads();
+        __syncthreads();
+        return;
+      }
     }
     f32x4 s[4][2];
     qk_tile<DK, DV>(s, qf, kcur, la);
@@ -506,6 +519,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const int klen = clamp_klen(k_len, b, Nk);
   int qrow[2];
   ft.qrow0 = q0 + wave * 32 + r16;
+  ft.wfirst = q0 + wave * 32;
+  ft.wlast = min(ft.wfirst + 31, Nq - 1);
   ft.klen = klen;
   ft.mr = mr;
 #pragma unroll
