@@ -49,6 +49,8 @@
 // one generator call; in the dK/dV kernel a lane holds one key of 16 rows,
 // so each thread generates one call per query tile (row tid / 4, group
 // tid % 4) into LDS, a tile ahead, and lanes read back the bytes they need.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_dropout.h"
 #include "fa_mask.h"
@@ -199,9 +201,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int t_end = kend > kbeg ? (kend + kTile - 1) / kTile : t_begin;
   const int t_full = (key_lo(mr, last_row) + kTile - 1) / kTile;
   const int t_full_end = key_end(mr, q0, klen) / kTile;
+  // a wave with a row past Nq or without an allowed key masks every tile
+  const bool wave_all_live = __builtin_amdgcn_ballot_w64(!(live[0] && live[1])) == 0;
 
   // key tile t (in kt, vt) while tile t + 1 loads into kn, vn
-  auto tile = [&](int t, const lds_char* kt, const lds_char* vt, lds_char* kn, lds_char* vn) {
+  auto tile = [&](auto mask_c, int t, const lds_char* kt, const lds_char* vt, lds_char* kn, lds_char* vn) {
+    constexpr bool masked = decltype(mask_c)::value;
     wait_loads();
     __syncthreads();  // tile t visible; tile t-1's buffers free
     const int j0 = t * kTile;
@@ -209,7 +214,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
       load_tile<DK>(kh, j0 + kTile, ka.ld, kn, wave);
       load_tile<DV>(vh, j0 + kTile, va.ld, vn, wave);
     }
-    const bool tile_masked = t < t_full || t >= t_full_end || BIAS;
     // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of row[qb]
     f32x4 s[4][2], dp[4][2];
 #pragma unroll
@@ -233,7 +237,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     // written over s
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const bool masked = tile_masked || !live[qb];
       Philox4 zw;
       if (DROP) zw = dropout_words(dsp, row[qb], t, (uint32_t)bh, g);
 #pragma unroll
@@ -270,9 +273,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     load_tile<DK>(kh, t_begin * kTile, ka.ld, K0, wave);
     load_tile<DV>(vh, t_begin * kTile, va.ld, V0, wave);
   }
-  for (int t = t_begin; t < t_end; t += 2) {
-    tile(t, K0, V0, K1, V1);
-    if (t + 1 < t_end) tile(t + 1, K1, V1, K0, V0);
+  // Tile t sits in buffer (t - t_begin) & 1.  Tiles [t_full, t_full_end)
+  // need no mask (unless there is a bias, or a row of the wave is past Nq
+  // or sees no key); the unmasked run starts at an even distance from
+  // t_begin, in buffer 0 (a tile moved into a masked run is still computed
+  // correctly).
+  const std::true_type mask_on;
+  const std::false_type mask_off;
+  const bool any_full = !BIAS && wave_all_live;
+  int tf = any_full ? min(max(t_full, t_begin), t_end) : t_end;
+  tf = min(tf + ((tf - t_begin) & 1), t_end);
+  const int tfe = any_full ? max(min(t_full_end, t_end), tf) : tf;
+  int t = t_begin;
+  for (; t < tf; ++t) {
+    if ((t - t_begin) & 1)
+      tile(mask_on, t, K1, V1, K0, V0);
+    else
+      tile(mask_on, t, K0, V0, K1, V1);
+  }
+  for (; t + 1 < tfe; t += 2) {
+    tile(mask_off, t, K0, V0, K1, V1);
+    tile(mask_off, t + 1, K1, V1, K0, V0);
+  }
+  if (t < tfe) {
+    tile(mask_off, t, K0, V0, K1, V1);
+    ++t;
+  }
+  for (; t < t_end; ++t) {
+    if ((t - t_begin) & 1)
+      tile(mask_on, t, K1, V1, K0, V0);
+    else
+      tile(mask_on, t, K0, V0, K1, V1);
   }
 
 #pragma unroll
