@@ -198,6 +198,12 @@ BWD_CASES = [
     (2, 1, 150, 260, 128, 64, True, False, [260, 90], "top_left", 40, None, 200),
     (1, 2, 96, 160, 64, 128, False, True, None, "bottom_right", 30, 25, 128),
     (1, 1, 77, 100, 40, 24, True, False, None, "bottom_right", 20, None, 180),   # general kernels
+    # no bias, no dropout, several 64-row query tiles: the dK/dV kernel's
+    # unmasked run of query tiles lies between masked ones
+    (1, 2, 700, 900, 128, 128, True, False, None, "bottom_right", 200, None, 256),
+    (2, 2, 640, 640, 128, 128, True, False, [640, 333], "top_left", 150, None, 256),
+    (1, 2, 520, 800, 64, 64, False, False, None, "bottom_right", 130, 70, 256),
+    (1, 1, 1000, 1000, 128, 128, True, False, None, "bottom_right", None, None, 256),
 ]
 
 
