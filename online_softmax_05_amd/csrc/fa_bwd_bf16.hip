@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char qb1[Tile<DK>::BYTES];
   __shared__ __attribute__((aligned(1024))) char gb0[Tile<DV>::BYTES];
   __shared__ __attribute__((aligned(1024))) char gb1[Tile<DV>::BYTES];
-  __shared__ float lbuf[2][kTile];      // L_i log2 e (0 for rows without a key)
-  __shared__ float cbuf[2][kTile];      // c_i
+  __shared__ __attribute__((aligned(16))) float lbuf[2][kTile];  // L_i log2 e (0 for rows without a key)
+  __shared__ __attribute__((aligned(16))) float cbuf[2][kTile];  // c_i
   __shared__ int lobuf[2][kTile];       // per row: first visible key
   __shared__ unsigned spbuf[2][kTile];  // per row: number of visible keys (0 for rows without a key)
   // dropout words of the query tile: row rr, group g', word w at
@@ -463,18 +463,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
       for (int i = 0; i < DV / 32; ++i) dp[rb] = mfma(frag_read(gt_l + ga.frag[i] + 16 * rb * Tile<DV>::ROW), vf[i], dp[rb]);
     }
     f32x4 pv[4], dsv[4];
+    const auto p_and_d = [&](auto mask_t) {
+      constexpr bool mtest = decltype(mask_t)::value;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+      // the four rows 16rb + 4g .. +3 of this lane: one 16-byte read each
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&lbuf[par][16 * rb + 4 * g]);
+      const f32x4 cv = *reinterpret_cast<const f32x4*>(&cbuf[par][16 * rb + 4 * g]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 16 * rb + 4 * g + j;  // row within the tile
-        float arg = fmaf(s[rb][j], c2, -lbuf[par][rr]);
+        float arg = fmaf(s[rb][j], c2, -lv[j]);
         if (BIAS) {
           const int r = min(q0 + rr, Nq - 1);
           arg = fmaf(bias[(bh * Nq + r) * (size_t)Nk + min(key, Nk - 1)], kLog2e, arg);
         }
         float p = fast_exp2(arg);
-        if (masked && (unsigned)(key - lobuf[par][rr]) >= spbuf[par][rr]) p = 0.f;
+        if (mtest && (unsigned)(key - lobuf[par][rr]) >= spbuf[par][rr]) p = 0.f;
         float zr = 1.f;
         if (DROP) {
           // byte r16 % 4 of word `wave` of row rr's call for group r16 / 4
@@ -482,9 +487,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
           zr = dropout_keep(w, r16 & 3, dsp.keep) ? drop_scale : 0.f;
         }
         pv[rb][j] = zr * p;
-        dsv[rb][j] = p * (zr * dp[rb][j] - cbuf[par][rr]);
+        dsv[rb][j] = p * (zr * dp[rb][j] - cv[j]);
       }
     }
+    };
+    if (masked)
+      p_and_d(std::true_type{});
+    else
+      p_and_d(std::false_type{});
     // dV^T += G^T P and dK^T += Q^T D over the tile's two 32-row steps
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
