@@ -214,6 +214,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
       load_tile<DK>(kh, j0 + kTile, ka.ld, kn, wave);
       load_tile<DV>(vh, j0 + kTile, va.ld, vn, wave);
     }
+    // a masked tile that none of this wave's rows can see adds nothing to
+    // dQ (all its P are zero): skip its products (the row ranges only grow
+    // with the row, so the first row's lowest key and the last row's end
+    // bound them all)
+    if (masked) {
+      const int wfirst = q0 + 32 * wave, wlast = min(wfirst + 31, Nq - 1);
+      const bool dead = wlast < wfirst || key_end(mr, wlast, klen) <= j0 || key_lo(mr, wfirst) >= j0 + kTile;
+      if (__builtin_amdgcn_readfirstlane((int)dead)) return;
+    }
     // S^T and dP^T: key block kb, a lane holds keys 16kb + 4g + j of row[qb]
     f32x4 s[4][2], dp[4][2];
 #pragma unroll
