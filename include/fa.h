@@ -74,7 +74,9 @@ typedef enum {
  *   v     [B, H, Nk, dv]  dtype        read only (may be NULL if Nk == 0)
  *   bias  [B, H, Nq, Nk]  fp32 or NULL; added after scaling, before masking;
  *                                      must be finite at allowed positions
- *   k_len [B] int32 or NULL (NULL: every sequence has Nk keys)
+ *   k_len [B] int32 or NULL (NULL: every sequence has Nk keys); rows
+ *                                      j >= k_len[b] of k and v are never
+ *                                      read (their contents do not matter)
  *   o     [B, H, Nq, dv]  dtype        written in full
  *   lse   [B, H, Nq] fp32 or NULL      natural-log log-sum-exp per row
  *   1 <= dk, dv <= 128; B, H, Nq, Nk >= 0.  B*H*Nq == 0 is a no-op (FA_OK,
@@ -265,7 +267,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
  *   dout       [B, H, Nq, dv] dtype: dLoss/dO           read only
  *   lse        [B, H, Nq] fp32: fa_fwd's lse, required  read only
  *   bias, k_len, scale, causal: exactly as passed to fa_fwd (the bias is a
- *              fixed input: no bias gradient is formed)
+ *              fixed input: no bias gradient is formed); as in fa_fwd,
+ *              rows j >= k_len[b] of k and v are never read
  *   dq [B, H, Nq, dk], dk [B, H, Nk, dk], dv [B, H, Nk, dv]  dtype,
  *              written in full (keys no row can see get zero)
  *   workspace: device buffer of at least fa_bwd_workspace_bytes(B, H, Nq)

@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_general_kernel(
   Geom g{Nq, Nk, clamp_klen(k_len, b, Nk), mr, scale, bias == nullptr ? nullptr : bias + bh * Nq * (size_t)Nk,
          dsp, drop_scale, (uint32_t)bh};
 
-  load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, Nk, DK);
-  load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, Nk, DV);
+  load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, g.klen, DK);
+  load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, g.klen, DV);
 
   // this thread's outputs: key kk, dims sub + 8m
   const int kk = threadIdx.x >> 3, sub = threadIdx.x & 7;
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_general_kernel(
   const int kend = key_end(mr, min(r0 + kRows, Nq) - 1, g.klen);
   for (int j0 = (kbeg / kKeys) * kKeys; j0 < kend; j0 += kKeys) {
     __syncthreads();
-    load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, Nk, DK);
-    load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, Nk, DV);
+    load_rows(t.ks, DK + 1, k + bh * Nk * DK, j0, kKeys, g.klen, DK);
+    load_rows(t.vs, DV + 1, v + bh * Nk * DV, j0, kKeys, g.klen, DV);
     __syncthreads();
     pd_block(t, g, r0, j0, DK, DV);
     __syncthreads();

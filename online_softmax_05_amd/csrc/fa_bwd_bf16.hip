@@ -141,8 +141,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   TileAddr<DV> va;
   ka.init(lane, wave);
   va.init(lane, wave);
-  const HeadBuf kh = head_buf(k + bh * Nk * DK, (uint32_t)Nk * DK * 2);
-  const HeadBuf vh = head_buf(v + bh * Nk * DV, (uint32_t)Nk * DV * 2);
+  // rows at or past the key length read as zeros (never from memory)
+  const HeadBuf kh = head_buf(k + bh * Nk * DK, (uint32_t)klen * DK * 2);
+  const HeadBuf vh = head_buf(v + bh * Nk * DV, (uint32_t)klen * DV * 2);
   const float c2 = scale * kLog2e;
 
   // Each wave holds 32 query rows as two 16-row blocks qb: every K or V
@@ -369,7 +370,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   const int j0 = tc.qt * kTile;
   const int klen = clamp_klen(k_len, b, Nk);
   const int key = j0 + 16 * wave + r16;  // this lane's key
-  const bool kvalid = key < Nk;
+  const bool kvalid = key < Nk;    // dK, dV rows written (zero past the key length)
+  const bool kread = key < klen;   // K, V rows read: none at or past the key length
 
   TileAddr<DK> qa;
   TileAddr<DV> ga;
@@ -379,8 +381,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_kernel(
   const HeadBuf gh = head_buf(dout + bh * Nq * DV, (uint32_t)Nq * DV * 2);
 
   bf16x8 kf[DK / 32], vf[DV / 32];
-  load_rows_b<DK>(kf, k + bh * Nk * DK, key, kvalid, g);
-  load_rows_b<DV>(vf, v + bh * Nk * DV, key, kvalid, g);
+  load_rows_b<DK>(kf, k + bh * Nk * DK, key, kread, g);
+  load_rows_b<DV>(vf, v + bh * Nk * DV, key, kread, g);
   const float c2 = scale * kLog2e;
 
   f32x4 acc_v[DV / 16], acc_k[DK / 16];

@@ -216,8 +216,12 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
 
   TileAddr<kD> ta;
   ta.init(lane, wave);
-  const HeadBuf kh = head_buf(k + bh * Nk * kD, (uint32_t)Nk * kD * 2);
-  const HeadBuf vh = head_buf(v + bh * Nk * kD, (uint32_t)Nk * kD * 2);
+  // the buffers end at the sequence's key length: rows at or past k_len[b]
+  // fail the hardware range check and arrive as zeros, so the cache beyond
+  // the sequence is never read (whatever it holds, even NaN, cannot reach
+  // the P V products through a zero weight)
+  const HeadBuf kh = head_buf(k + bh * Nk * kD, (uint32_t)klen * kD * 2);
+  const HeadBuf vh = head_buf(v + bh * Nk * kD, (uint32_t)klen * kD * 2);
 
   float m = kNegInf, l = 0.f;  // this wave's state for row r16 (l: this lane's share)
   f32x4 o[kD / 16];            // O^T: dims 16db + 4g + j of row r16

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   Prefetch<DK, DV, BN> pf;
   if (t_begin < t_end) {
-    fetch_tile<DK, DV, BN>(pf, kbh, vbh, t_begin * BN, Nk, dk, dv, vec_k != 0, vec_v != 0, tid);
+    fetch_tile<DK, DV, BN>(pf, kbh, vbh, t_begin * BN, klen, dk, dv, vec_k != 0, vec_v != 0, tid);
     store_tile<DK, DV, BN>(pf, smem + (t_begin & 1) * T::BUF, tid);
   }
   __syncthreads();
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* ks = smem + (it & 1) * T::BUF;
     const uint16_t* vt = ks + T::K_ELEMS;
     const bool has_next = it + 1 < t_end;
-    if (has_next) fetch_tile<DK, DV, BN>(pf, kbh, vbh, n0 + BN, Nk, dk, dv, vec_k != 0, vec_v != 0, tid);
+    if (has_next) fetch_tile<DK, DV, BN>(pf, kbh, vbh, n0 + BN, klen, dk, dv, vec_k != 0, vec_v != 0, tid);
 
     // ---- S^T = K Q^T for this wave's 32 rows and BN keys ----------------
     f32x16 s[BN / 32];

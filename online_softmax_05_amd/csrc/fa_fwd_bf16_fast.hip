@@ -486,21 +486,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   const size_t bh = (size_t)tc.bh;
   const uint16_t* qbh = q + bh * Nq * DK;
 
+  // The K and V buffers end at the sequence's key length: rows at or past
+  // it fail the hardware range check and arrive as zeros, so they are never
+  // read from memory (a non-finite value stored there cannot reach P V
+  // through a zero weight).  Without key lengths there is nothing to wait
+  // for; with them the first tile waits for one scalar load.
+  const int klen = clamp_klen(k_len, b, Nk);
   FwdTile<DK, DV, BIAS, DROP> ft;
   ft.dsp = dsp;
   ft.bh = (uint32_t)tc.bh;
-  ft.kbuf = head_buf(k + bh * Nk * DK, (uint32_t)Nk * DK * 2);
-  ft.vbuf = head_buf(v + bh * Nk * DV, (uint32_t)Nk * DV * 2);
+  ft.kbuf = head_buf(k + bh * Nk * DK, (uint32_t)klen * DK * 2);
+  ft.vbuf = head_buf(v + bh * Nk * DV, (uint32_t)klen * DV * 2);
   ft.nk = Nk;
   ft.vec_bias = vec_bias;
   ft.g = g;
   ft.la.init(lane, wave);
 
   // The first K/V tile and Q load together, before anything waits on
-  // memory (the key length, the mask range): the start of a work-group then
-  // costs one memory latency.  The first tile's rows begin at the first
-  // row's lowest visible key, which the key length does not move; a query
-  // tile left with no key tile ignores the loaded tile.
+  // memory (other than the key length, when given): the start of a
+  // work-group then costs one memory latency.  The first tile's rows begin
+  // at the first row's lowest visible key, which the key length does not
+  // move; a query tile left with no key tile ignores the loaded tile.
   const int t_begin = key_lo(mr, q0) / kBN;
   const bool t0_in = t_begin < (Nk + kBN - 1) / kBN;
   if (t0_in) {
@@ -516,7 +522,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
       qw[qb][t] = load_q16(qbh, (uint32_t)Nq * DK * 2, (row * DK + 32 * t + 8 * g) * 2);
   }
 
-  const int klen = clamp_klen(k_len, b, Nk);
   int qrow[2];
   ft.qrow0 = q0 + wave * 32 + r16;
   ft.wfirst = q0 + wave * 32;

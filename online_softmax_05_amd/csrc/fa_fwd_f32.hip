@@ -125,14 +125,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
     for (int id = tid; id < BN * DK / 4; id += kThreads) {
       const int row = id / (DK / 4), c = id % (DK / 4);
       const int key = n0 + row;
-      f32x4 w = (key < Nk) ? load_row4(kbh + (size_t)key * dk, 4 * c, dk, vec_k != 0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 w = (key < klen) ? load_row4(kbh + (size_t)key * dk, 4 * c, dk, vec_k != 0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) ks[row * T::KS + 4 * c + e] = w[e];
     }
     for (int id = tid; id < BN * DV / 4; id += kThreads) {
       const int row = id / (DV / 4), c = id % (DV / 4);
       const int key = n0 + row;
-      f32x4 w = (key < Nk) ? load_row4(vbh + (size_t)key * dv, 4 * c, dv, vec_v != 0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 w = (key < klen) ? load_row4(vbh + (size_t)key * dv, 4 * c, dv, vec_v != 0) : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(vs + row * T::VS + 4 * c) = w;
     }
     __syncthreads();
