@@ -193,6 +193,34 @@ int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
                      void* stream);
 
 /*
+ * fa_decode_splitk_static -- fa_decode_splitk for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * fa_decode_splitk (the same kernels run), without the workspace: the
+ * partial states live in a static device array of the library,
+ * FA_STATIC_SCRATCH_BYTES per GPU, loaded with the library's code object and
+ * held until the process ends.  The call allocates and frees nothing.
+ *
+ *   Returns FA_ERR_WORKSPACE when the partial states of the call,
+ *   fa_decode_splitk_workspace_bytes(B, H, Nk_max, dv, chunk), exceed
+ *   FA_STATIC_SCRATCH_BYTES (e.g. B * H = 2048 sequence-heads of 8192 keys
+ *   in 512-key chunks with dv = 128 need 17 MB); other errors as
+ *   fa_decode_splitk.  The array's device address is looked up once per
+ *   device, on the first call made while that device is current.
+ *   All calls on one GPU share the array: calls ordered on one stream are
+ *   safe, calls that overlap in time on one GPU (two streams, two host
+ *   threads) race on it and give undefined results.  Nothing in the array
+ *   needs clearing between calls (every state the merge reads is written
+ *   by the same call).
+ */
+#define FA_STATIC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int fa_decode_splitk_static(const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* k_len,
+                            void* o, float* lse, int B, int H, int Nk_max,
+                            int dk, int dv, int chunk, int dtype, float scale,
+                            void* stream);
+
+/*
  * Bytes of fp32 workspace fa_decode_splitk_mq needs:
  *   B * H * ceil(Nk_max / chunk) * Nq * (dv + 2) * 4.
  * Returns 0 for invalid arguments (negative sizes, Nq outside 1..16, chunk

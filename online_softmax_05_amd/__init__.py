@@ -27,6 +27,7 @@ __all__ = [
     "fa_fwd", "fa_fwd_ex", "fa_decode_splitk", "fa_decode_splitk_workspace_bytes",
     "fa_check_fwd", "fa_check_fwd_ex", "fa_check_decode", "fa_bwd_ex", "fa_check_bwd_ex", "keep_256_for", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd",
     "fa_decode_splitk_mq", "fa_decode_splitk_mq_workspace_bytes", "fa_check_decode_mq",
+    "fa_decode_splitk_static", "FA_STATIC_SCRATCH_BYTES",
     "fa_status_str", "fa_abi_version",
 ]
 
@@ -34,6 +35,7 @@ FA_F32 = 0
 FA_BF16 = 1
 FA_ALIGN_BOTTOM_RIGHT = 0
 FA_ALIGN_TOP_LEFT = 1
+FA_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024  # include/fa.h
 _ALIGN = {"bottom_right": FA_ALIGN_BOTTOM_RIGHT, "top_left": FA_ALIGN_TOP_LEFT}
 _STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
            4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP"}
@@ -58,6 +60,7 @@ _SIGNATURES = {
     "fa_decode_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitk": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_check_decode": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz]),
+    "fa_decode_splitk_static": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_decode_splitk_mq_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "fa_decode_splitk_mq": (_i, [_vp, _vp, _vp, _ip, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                  _vp]),
@@ -292,6 +295,40 @@ def fa_decode_splitk(q, k_cache, v_cache, k_len, *, scale=None, chunk=512, out=N
     st = lib().fa_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_len), _ptr(out), _ptr(lse),
                                 B, H, Nk, dk, dv, int(chunk), _dtype_code(q), float(scale),
                                 _ptr(workspace), workspace.numel() * 4, _stream(dev))
+    if st != 0:
+        raise FaError(st)
+    return out, lse
+
+
+def fa_decode_splitk_static(q, k_cache, v_cache, k_len, *, out, lse=None, scale=None, chunk=512):
+    """fa_decode_splitk without a workspace, for callers that cannot allocate:
+    the partial states live in the library's static device scratch
+    (FA_STATIC_SCRATCH_BYTES per GPU).  The caller passes the outputs
+    (o [B,H,dv] in q's dtype; lse fp32 [B,H] or None); nothing is allocated
+    here.  Calls that overlap in time on one GPU race on the scratch.
+    Returns (out, lse)."""
+    _need(q, "q", dims=3)
+    dev = q.device
+    _need(k_cache, "k_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(v_cache, "v_cache", dtype=q.dtype, dims=4, device=dev)
+    _need(k_len, "k_len", dtype=torch.int32, dims=1, device=dev)
+    B, H, dk = q.shape
+    Nk, dv = k_cache.shape[2], v_cache.shape[3]
+    if tuple(k_cache.shape) != (B, H, Nk, dk) or tuple(v_cache.shape) != (B, H, Nk, dv):
+        raise FaError(2, "cache shapes do not match q")
+    if k_len.shape[0] != B:
+        raise FaError(2, f"k_len must have {B} entries")
+    _need(out, "out", dtype=q.dtype, dims=3, device=dev)
+    if tuple(out.shape) != (B, H, dv):
+        raise FaError(2, f"out must have shape {(B, H, dv)}")
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, dims=2, device=dev)
+        if tuple(lse.shape) != (B, H):
+            raise FaError(2, f"lse must have shape {(B, H)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    st = lib().fa_decode_splitk_static(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_len), _ptr(out), _ptr(lse),
+                                       B, H, Nk, dk, dv, int(chunk), _dtype_code(q), float(scale), _stream(dev))
     if st != 0:
         raise FaError(st)
     return out, lse

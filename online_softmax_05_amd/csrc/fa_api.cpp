@@ -194,7 +194,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 extern "C" {
 
-int fa_abi_version(void) { return 104; }
+int fa_abi_version(void) { return 105; }
 
 const char* fa_status_str(int status) {
   switch (status) {
@@ -203,7 +203,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_SHAPE: return "invalid or too large shape";
     case FA_ERR_UNSUPPORTED:
       return "unsupported dtype, head dim, block_n, chunk, causal flag, alignment, window, dropout keep or scale";
-    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small (static scratch: the call needs more than FA_STATIC_SCRATCH_BYTES)";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -275,6 +275,24 @@ int fa_decode_splitk(const void* q, const void* k_cache, const void* v_cache, co
   const hipError_t e = dtype == FA_BF16 ? fa::launch_decode_bf16(a, static_cast<hipStream_t>(stream))
                                         : fa::launch_decode_f32(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_splitk_static(const void* q, const void* k_cache, const void* v_cache, const int32_t* k_len,
+                            void* o, float* lse, int B, int H, int Nk_max, int dk, int dv, int chunk, int dtype,
+                            float scale, void* stream) {
+  // host checks first (no GPU call): the states must fit the static array,
+  // which then stands in for the workspace in the usual argument checks
+  const size_t need = fa_decode_splitk_workspace_bytes(B, H, Nk_max, dv, chunk);
+  if (need > FA_STATIC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t{256});  // aligned, never dereferenced
+  int st = check_decode(q, k_cache, v_cache, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, placeholder,
+                        FA_STATIC_SCRATCH_BYTES);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0) return FA_OK;
+  void* scratch = nullptr;
+  if (fa::static_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  return fa_decode_splitk(q, k_cache, v_cache, k_len, o, lse, B, H, Nk_max, dk, dv, chunk, dtype, scale, scratch,
+                          FA_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t fa_decode_splitk_mq_workspace_bytes(int B, int H, int Nq, int Nk_max, int dv, int chunk) {

@@ -90,6 +90,9 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+// Device address of the library's static scratch array on the current
+// device (looked up once per device; fa_scratch.hip).
+hipError_t static_scratch(void** out);
 hipError_t launch_decode_mq_bf16(const DecodeMqArgs& a, hipStream_t stream);
 hipError_t launch_decode_mq_f32(const DecodeMqArgs& a, hipStream_t stream);
 // backward: c = dO.O, then dK/dV and dQ (bf16 with head dims 64/128 and

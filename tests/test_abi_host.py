@@ -60,7 +60,7 @@ def test_header_is_plain_c():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 104
+    assert fa.fa_abi_version() == 105
     for st in range(6):
         assert isinstance(fa.fa_status_str(st), str) and fa.fa_status_str(st)
     assert fa.fa_status_str(0) == "ok"
@@ -287,3 +287,34 @@ def test_binding_fails_loudly_without_a_device():
     q = torch.zeros(1, 1, 4, 8)
     with pytest.raises(fa.FaError):
         fa.fa_fwd(q, q, q)
+
+
+def static_decode(**kw):
+    """fa_decode_splitk_static with fake pointers: every case here is rejected
+    (or is a no-op) on the host, before the scratch lookup or any launch."""
+    a = dict(q=P, k=P, v=P, k_len=P, o=P, lse=P, B=4, H=8, Nk=1000, dk=128, dv=128, chunk=512,
+             dtype=fa.FA_BF16, scale=0.125)
+    a.update(kw)
+    return fa.lib().fa_decode_splitk_static(a["q"], a["k"], a["v"], a["k_len"], a["o"], a["lse"], a["B"], a["H"],
+                                           a["Nk"], a["dk"], a["dv"], a["chunk"], a["dtype"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    # partial states beyond the static scratch: 64 x 64 sequence-heads x 16 chunks x 130 floats = 34 MB
+    ({"B": 64, "H": 64, "Nk": 8192}, WS),
+    ({"B": 64, "H": 128, "Nk": 8192, "chunk": 1024}, WS),   # 8192 x 8 x 130 x 4 = 34 MB
+    ({"chunk": 100}, UNSUP), ({"dk": 129}, UNSUP), ({"dtype": 7}, UNSUP),
+    ({"q": None}, NULL), ({"k_len": None}, NULL), ({"o": None}, NULL),
+    ({"B": -1}, SHAPE),
+    ({"B": 0, "q": None, "o": None}, OK),     # nothing to compute: no scratch lookup, no launch
+])
+def test_static_decode_host_checks(kw, want):
+    assert fa.FA_STATIC_SCRATCH_BYTES == 32 * 1024 * 1024
+    assert static_decode(**kw) == want
+
+
+def test_static_decode_limit_matches_workspace_size():
+    # the decode workload (64 x 32 sequence-heads, 8192 keys, 512-key chunks,
+    # dv 128) fits; twice its heads do not
+    assert fa.fa_decode_splitk_workspace_bytes(64, 32, 8192, 128, 512) <= fa.FA_STATIC_SCRATCH_BYTES
+    assert fa.fa_decode_splitk_workspace_bytes(64, 64, 8192, 128, 512) > fa.FA_STATIC_SCRATCH_BYTES
