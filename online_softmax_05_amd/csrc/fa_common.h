@@ -53,6 +53,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// Sum of the two bf16 values packed in w, added to acc in fp32
+// (v_dot2c_f32_bf16 against the pair (1, 1): both products are exact).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // Work-group -> (batch*head, tile) mapping: query tiles in the forward and
 // dQ kernels, key tiles in the dK/dV kernel.
 //

@@ -226,6 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
   float m_run = kNegInf;  // running max (base 2), shared by both lane halves
   float l_run = 0.f;      // this lane half's part of the running denominator
+  float lu_run = 0.f;     // the same over the bf16-rounded weights that multiply V
 
   Prefetch<DK, DV, BN> pf;
   if (t_begin < t_end) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     m_run = m_new;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
 
-    float psum = 0.f;
+    float psum = 0.f, usum = 0.f;
     bf16x8 pb[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -348,11 +349,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           const float p1 = fast_exp2(BIAS ? s[kb][r1] + xo[r1] : fmaf(s[kb][r1], c, -m_use));
           psum += p0 + p1;
           w[e / 2] = pack_bf16x2((km >> r0) & 1u ? p0 : 0.f, (km >> r1) & 1u ? p1 : 0.f);
+          usum = add_bf16_pair(w[e / 2], usum);  // used only without dropout (then nothing is zeroed)
         }
         pb[kb * 2 + t2] = __builtin_bit_cast(bf16x8, w);
       }
     }
     l_run = fmaf(alpha, l_run, psum);
+    lu_run = fmaf(alpha, lu_run, usum);
 
     // rescale u only when some row of the wave moved its reference
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -378,9 +381,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // ---- epilogue: divide once; empty rows get o = 0, lse = -inf ------------
   const float l_tot = half_swap_sum(l_run);
+  // without dropout O is divided by the sum of the bf16-rounded weights it
+  // was built from (an exact weighted mean of V up to fp32 rounding); lse
+  // and the dropout divisor use the unrounded sum
+  const float l_used = half_swap_sum(lu_run);
   if (!row_valid) return;
   const bool nonempty = l_tot > 0.f;
-  const float inv = nonempty ? drop_scale / l_tot : 0.f;
+  const float inv = nonempty ? drop_scale / (dsp.keep >= 256 ? l_used : l_tot) : 0.f;
   uint16_t* orow = o + (bh * Nq + qi) * (size_t)dv;
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) {

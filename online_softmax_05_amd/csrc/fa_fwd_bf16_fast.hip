@@ -240,9 +240,11 @@ __device__ __forceinline__ void qk_tile(f32x4 (&s)[4][2], const QFrag<DK>& q, co
 }
 
 struct RowState {
-  float m[2];  // reference maximum (base 2) per query block
-  float l[2];  // this lane's share (4 of the 64 keys of each tile) of the denominator
+  float m[2];   // reference maximum (base 2) per query block
+  float l[2];   // this lane's share (4 of the 64 keys of each tile) of the denominator
+  float lu[2];  // the same share summed over the bf16-rounded weights that multiply V
 };
+
 
 // O^T += V^T P^T for one tile: k-step kt covers keys 32kt .. 32kt+31, slot
 // s of lane group g holding key 32kt + 16(s/4) + 4g + s%4.
@@ -326,7 +328,7 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float psum = 0.f;
+    float psum = 0.f, usum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       u32x4 w;
@@ -349,10 +351,12 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
         }
         w[2 * h] = cvt_pk_bf16(p[0], p[1]);
         w[2 * h + 1] = cvt_pk_bf16(p[2], p[3]);
+        if (!DROP) usum = add_bf16_pair(w[2 * h + 1], add_bf16_pair(w[2 * h], usum));
       }
       pb[kt][qb] = __builtin_bit_cast(bf16x8, w);
     }
     st.l[qb] = fmaf(alpha[qb], st.l[qb], psum);
+    if (!DROP) st.lu[qb] = fmaf(alpha[qb], st.lu[qb], usum);
   }
   return __builtin_amdgcn_ballot_w64(any_grow) != 0;
 }
@@ -554,6 +558,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
   }
   ft.st.m[0] = ft.st.m[1] = kNegInf;
   ft.st.l[0] = ft.st.l[1] = 0.f;
+  ft.st.lu[0] = ft.st.lu[1] = 0.f;
   wait_loads();
   __syncthreads();
   {
@@ -606,9 +611,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = quad_sum(ft.st.l[qb]);
+    // O is divided by the sum of the weights it was built from (the
+    // bf16-rounded ones), so it is an exact weighted mean of the values up
+    // to fp32 rounding: a row dominated by one key then returns that key's
+    // value instead of carrying the key's own rounding (up to 2^-9 of |v|).
+    // lse keeps the sum of the unrounded weights.  With dropout the
+    // divisor stays the unrounded sum of the undropped weights.
+    const float l_out = DROP ? l_tot : quad_sum(ft.st.lu[qb]);
     if (!ft.rvalid[qb]) continue;
     const bool nonempty = l_tot > 0.f;
-    const float inv = nonempty ? (DROP ? drop_scale : 1.f) / l_tot : 0.f;
+    const float inv = nonempty ? (DROP ? drop_scale : 1.f) / l_out : 0.f;
     uint16_t* orow = o + (bh * Nq + qrow[qb]) * (size_t)DV;
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {

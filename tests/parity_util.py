@@ -92,3 +92,78 @@ def oracle_rows(q, k, v, rows, *, scale, causal, k_len=None, bias=None, align="b
             o[n] = ob[j]
             lse[n] = lb[j]
     return o, lse
+
+
+def _blas_limit(n):
+    try:
+        from threadpoolctl import threadpool_limits
+
+        return threadpool_limits(limits=n, user_api="blas")
+    except Exception:  # noqa: BLE001
+        import contextlib
+
+        return contextlib.nullcontext()
+
+
+def compare_every_head(o_gpu, lse_gpu, q, k, v, *, scale, causal, k_len_host=None, nq_rows=None, what,
+                       dtype=torch.bfloat16, workers=8, row_block=2048, window=(None, None), dropout=None,
+                       o_tol_factor=1.0):
+    """Every output element of a full-size launch against the oracle.
+
+    o_gpu [B,H,Nq,dv], lse_gpu [B,H,Nq] (device or host); q, k, v the exact
+    inputs (device or host).  The oracle runs head by head (complete rows of
+    S in blocks of ``row_block`` rows), ``workers`` heads at a time on host
+    threads (numpy releases the interpreter lock inside its large array
+    operations; BLAS is limited to one thread per worker).  With
+    ``k_len_host`` the keys of sequence b are truncated to k_len[b] before the
+    call, for the decode entry points whose causal alignment is against the
+    sequence's own length.  Max-abs errors over all elements at the dtype's
+    tolerance (the o bound times ``o_tol_factor``: the dropout tests' 256/keep);
+    ``window`` and ``dropout`` as for the oracle; rows with lse_ref = -inf
+    must be exactly o = 0, lse = -inf.
+    Returns (max |do|, max |dlse|, number of rows compared)."""
+    import concurrent.futures
+
+    qh = q.detach().to("cpu")
+    kh = k.detach().to("cpu")
+    vh = v.detach().to("cpu")
+    og = o_gpu.detach().to("cpu").double().numpy()
+    lg = lse_gpu.detach().to("cpu").double().numpy()
+    B, H, Nq = qh.shape[0], qh.shape[1], qh.shape[2]
+    tol = dict(TOL[dtype])
+    tol["o"] *= o_tol_factor
+    sc = scale32(scale)
+
+    def head(bh):
+        b, h = divmod(bh, H)
+        n = kh.shape[2] if k_len_host is None else int(k_len_host[b])
+        qq = qh[b, h].double().numpy()
+        kk = kh[b, h, :n].double().numpy()
+        vv = vh[b, h, :n].double().numpy()
+        e_o = e_l = 0.0
+        for r0 in range(0, Nq, row_block):
+            r1 = min(Nq, r0 + row_block)
+            o_ref, l_ref = oracle.attention_head(qq[r0:r1], kk, vv, scale=sc, nq=Nq, causal=causal,
+                                                 row_ids=np.arange(r0, r1), window=window, dropout=dropout,
+                                                 bh=bh)
+            o, lse = og[b, h, r0:r1], lg[b, h, r0:r1]
+            emp = np.isneginf(l_ref)
+            if emp.any():
+                assert np.all(o[emp] == 0.0) and np.all(np.isneginf(lse[emp])), \
+                    f"{what}: empty rows of ({b}, {h}) must give o = 0, lse = -inf"
+            ne = ~emp
+            assert not np.isnan(o).any() and not np.isnan(lse).any(), f"{what}: NaN in ({b}, {h})"
+            if ne.any():
+                e_o = max(e_o, float(np.max(np.abs(o[ne] - o_ref[ne]))))
+                e_l = max(e_l, float(np.max(np.abs(lse[ne] - l_ref[ne]))))
+        return e_o, e_l
+
+    err_o = err_l = 0.0
+    with _blas_limit(1), concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for e_o, e_l in ex.map(head, range(B * H)):
+            err_o, err_l = max(err_o, e_o), max(err_l, e_l)
+    say(f"{what}: every element of {B * H} heads x {Nq} rows: max|do| = {err_o:.3e} (tol {tol['o']:.0e}), "
+        f"max|dlse| = {err_l:.3e} (tol {tol['lse']:.0e})")
+    assert err_o <= tol["o"], f"{what}: max |o - o_ref| = {err_o:.3e} > {tol['o']}"
+    assert err_l <= tol["lse"], f"{what}: max |lse - lse_ref| = {err_l:.3e} > {tol['lse']}"
+    return err_o, err_l, B * H * Nq

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity_util import compare, f64, say, scale32
+from tests.parity_util import compare, compare_every_head, f64, say, scale32
 
 pytestmark = pytest.mark.gpu
 
@@ -98,12 +98,11 @@ def test_decode_mq_single_row_matches_decode(dev):
     assert float((l1 - l2[:, :, 0]).abs().max()) <= 1e-3
 
 
-def test_decode_mq_full_size_sampled(dev):
+def test_decode_mq_full_size_every_row(dev):
     """The multi-query decode workload (64x32 sequences x 4 causal rows, caches
     of 8192 keys, lengths U{1..8192}, d128 bf16, 512-key chunks) in the launch
-    configuration the benchmark times: sampled (sequence, head) pairs -- the
-    shortest and the longest sequence among them -- against the oracle over
-    the truncated cache."""
+    configuration the benchmark times: every row of every (sequence, head)
+    against the oracle over the cache truncated to the sequence's length."""
     import online_softmax_05_amd as fa
 
     inp = workloads.decode_mq(dev)
@@ -112,14 +111,5 @@ def test_decode_mq_full_size_sampled(dev):
     o, lse = fa.fa_decode_splitk_mq(inp["q"], inp["k"], inp["v"], inp["k_len"], causal=True, scale=inp["scale"],
                                     chunk=inp["chunk"])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(17)
-    bs = sorted({int(kl.argmin()), int(kl.argmax())} | set(rng.integers(0, 64, 4).tolist()))
-    hs = [0, 31, int(rng.integers(1, 31))]
-    Nq = inp["q"].shape[2]
-    for b in bs:
-        n = int(kl[b])
-        for h in hs:
-            ob, lb = oracle.attention_head(f64(inp["q"][b, h]), f64(inp["k"][b, h, :n]), f64(inp["v"][b, h, :n]),
-                                           scale=scale32(inp["scale"]), nq=Nq, causal=True)
-            compare(o[b, h][None, None], lse[b, h][None, None], ob[None, None], lb[None, None], torch.bfloat16,
-                    f"decode mq full size (b={b}, h={h}, k_len={n})")
+    compare_every_head(o, lse, inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, k_len_host=kl,
+                       what="decode mq full size")

@@ -3,10 +3,9 @@ oracle, element by element, on the same seeded inputs.
 
 Tolerances (max abs over all compared elements): fp32 inputs 1e-5 for o and
 lse; bf16 inputs 2e-2 for o and 1e-3 for lse; empty rows exactly o = 0 and
-lse = -inf.  Small workloads are compared in full; the full-size prefill,
-long-context and decode workloads -- in the launch configuration the
-benchmark times -- are compared on sampled rows that the oracle computes one
-by one, plus properties that hold at any size.
+lse = -inf.  Every workload is compared in full: the full-size prefill,
+long-context and decode workloads too, in the launch configuration the
+benchmark times (the oracle runs head by head on host threads).
 """
 
 import math
@@ -18,7 +17,7 @@ import torch
 import oracle
 import workloads
 from tests import pins
-from tests.parity_util import TOL, compare, f64, oracle_full, oracle_rows, say, scale32
+from tests.parity_util import TOL, compare, compare_every_head, f64, oracle_full, say, scale32
 
 pytestmark = pytest.mark.gpu
 
@@ -298,24 +297,11 @@ def test_lse_optional_and_out_reuse(dev):
 
 
 # ---------------------------------------------------------------------------
-# full-size prefill and long-context workloads (sampled rows)
+# full-size prefill and long-context workloads: every output element
 # ---------------------------------------------------------------------------
 
-def _sample_rows(rng, B, H, N, n_random, tile=128):
-    rows = set()
-    special = [0, 1, 31, 32, 63, 64, tile - 1, tile, tile + 1, N // 2 - 1, N // 2, N - tile - 1, N - tile,
-               N - 2, N - 1]
-    for _ in range(n_random):
-        rows.add((int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, N))))
-    for i in special:
-        rows.add((int(rng.integers(0, B)), int(rng.integers(0, H)), i))
-    rows.add((B - 1, H - 1, N - 1))
-    rows.add((0, 0, 0))
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("name", ["prefill", "long"])
-def test_full_size_sampled(dev, name):
+def test_full_size_every_row(dev, name):
     import online_softmax_05_amd as fa
 
     say(f"{name}: drawing inputs on the device")
@@ -323,17 +309,9 @@ def test_full_size_sampled(dev, name):
     say(f"{name}: fa_fwd (the benchmark's launch configuration)")
     o, lse = fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True, block_n=inp["block_n"])
     torch.cuda.synchronize()
-    s = workloads.SHAPES[name]
-    B, H, N = s["B"], s["H"], s["Nq"]
-    rng = np.random.default_rng(7 if name == "prefill" else 8)
-    rows = _sample_rows(rng, B, H, N, 96 if name == "prefill" else 48)
-    say(f"{name}: oracle on {len(rows)} sampled rows")
-    o_ref, lse_ref = oracle_rows(inp["q"], inp["k"], inp["v"], rows, scale=inp["scale"], causal=True)
-    og = np.stack([f64(o[b, h, i]) for b, h, i in rows])
-    lg = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    compare(torch.from_numpy(og), torch.from_numpy(lg), o_ref, lse_ref, torch.bfloat16, f"{name} sampled rows")
-    # properties over every row: finite, and lse >= its own row's first logit
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    say(f"{name}: oracle on every row of every head")
+    compare_every_head(o, lse, inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True,
+                       what=f"{name} full size")
     # row 0 sees exactly key 0 (bottom-right causal, Nq == Nk): o = v_0, lse = s_00
     v0 = inp["v"][:, :, 0, :].float()
     assert torch.max(torch.abs(o[:, :, 0, :].float() - v0)).item() <= 1e-2
@@ -358,7 +336,7 @@ def _decode_oracle(q, k, v, k_len_host, pairs, scale):
     return o, lse
 
 
-def test_decode_full_size_sampled(dev):
+def test_decode_full_size_every_row(dev):
     import online_softmax_05_amd as fa
 
     say("decode: drawing inputs on the device")
@@ -367,17 +345,9 @@ def test_decode_full_size_sampled(dev):
     o, lse = fa.fa_decode_splitk(inp["q"], inp["k"], inp["v"], inp["k_len"], scale=inp["scale"],
                                  chunk=inp["chunk"])
     torch.cuda.synchronize()
-    kl = inp["k_len_host"]
-    rng = np.random.default_rng(55)
-    B, H = workloads.SHAPES["decode"]["B"], workloads.SHAPES["decode"]["H"]
-    pairs = sorted({(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(48)}
-                   | {(int(np.argmin(kl)), 0), (int(np.argmax(kl)), H - 1)})
-    say(f"decode: oracle on {len(pairs)} sampled (b, h)")
-    o_ref, lse_ref = _decode_oracle(inp["q"], inp["k"], inp["v"], kl, pairs, inp["scale"])
-    og = np.stack([f64(o[b, h]) for b, h in pairs])
-    lg = np.array([float(lse[b, h]) for b, h in pairs])
-    compare(torch.from_numpy(og), torch.from_numpy(lg), o_ref, lse_ref, torch.bfloat16, "decode sampled")
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    say("decode: oracle on every (sequence, head)")
+    compare_every_head(o[:, :, None], lse[:, :, None], inp["q"][:, :, None], inp["k"], inp["v"],
+                       scale=inp["scale"], causal=False, k_len_host=inp["k_len_host"], what="decode full size")
     del inp, o, lse
     torch.cuda.empty_cache()
 
