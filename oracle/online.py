@@ -18,12 +18,13 @@ definition under any key partition and visiting order.
       u = exp(m_A - m) u_A + exp(m_B - m) u_B.
   An empty block is skipped, never evaluated as exp(-inf - (-inf)) ([GS]
   section 6).
-* Sequential update ([GS] section 5; [OA] "Rescaling Both Accumulators When
-  the Maximum Increases"): per query tile, start from the empty state; for
-  every key tile and every row that has allowed keys in it, take the new
-  maximum, rescale the old l and u by exp(m_old - m_new), add the tile's mass
-  and weighted values; after the last tile divide once, o = u / l, and give an
-  empty row o = 0, lse = -inf ([GS] sections 5-7).
+* Sequential form ([GS] section 5; [VW] Step 5): because the merge is exact
+  and associative, a row's state after the key tiles visited so far is the
+  merge of those tiles' block states, taken one tile at a time in visiting
+  order from the empty state.  A tile in which the row has no allowed key
+  contributes no block.  The row's output is u / l of its final state and
+  lse = m + ln l; a row that never received a block is empty: o = 0,
+  lse = -inf ([GS] sections 5-7).
 """
 
 import numpy as np
@@ -102,36 +103,31 @@ def online_ref(q, k, v, *, scale, causal=False, k_len_b=None, bias=None,
     o = np.zeros((nq, dv))
     lse = np.full(nq, -np.inf)
     for qa, qb in query_tiles:
-        rows = qb - qa
-        m = np.full(rows, -np.inf)
-        ell = np.zeros(rows)
-        u = np.zeros((rows, dv))
+        states = [None] * (qb - qa)  # per row of the query tile; None = empty
         for t in order:
             ka, kb = key_tiles[t]
             # scaled scores and the mask by global position ([GS] section 6)
             s = (q[qa:qb] @ k[ka:kb].T) * float(scale)
             if bias is not None:
                 s = s + np.asarray(bias, dtype=np.float64)[qa:qb, ka:kb]
-            ok = allowed_mask(np.arange(qa, qb), nq, nk, causal,
-                              k_len_b)[:, ka:kb]
-            alphas = np.ones(rows)
-            for r in range(rows):
+            ok = allowed_mask(np.arange(qa, qb), nq, nk, causal, k_len_b)[:, ka:kb]
+            alphas = np.ones(qb - qa)
+            for r in range(qb - qa):
                 if not ok[r].any():
-                    continue  # no allowed key here: keep the state as it is
-                x = s[r, ok[r]]
-                m_new = max(m[r], x.max())
-                # the empty state has no mass to rescale ([GS] section 5)
-                alpha = np.exp(m[r] - m_new) if ell[r] > 0 else 0.0
-                e = np.exp(x - m_new)
-                ell[r] = alpha * ell[r] + e.sum()
-                u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]
-                m[r] = m_new
-                alphas[r] = alpha
+                    continue  # no allowed key in this tile: no block to merge
+                old = states[r]
+                states[r] = merge_states(old, block_state(s[r, ok[r]], v[ka:kb][ok[r]]))
+                # the factor the merge applied to the state held before
+                alphas[r] = 0.0 if old is None else np.exp(old[0] - states[r][0])
             if trace is not None:
                 trace.append({"query_tile": (qa, qb), "key_tile": (ka, kb),
-                              "m": m.copy(), "l": ell.copy(), "u": u.copy(),
+                              "m": np.array([-np.inf if x is None else x[0] for x in states]),
+                              "l": np.array([0.0 if x is None else x[1] for x in states]),
+                              "u": np.array([np.zeros(dv) if x is None else x[2] for x in states]),
                               "alpha": alphas})
-        nonempty = ell > 0
-        o[qa:qb][nonempty] = u[nonempty] / ell[nonempty, None]
-        lse[qa:qb][nonempty] = m[nonempty] + np.log(ell[nonempty])
+        for r, st in enumerate(states):
+            if st is not None:
+                m, ell, u = st
+                o[qa + r] = u / ell
+                lse[qa + r] = m + np.log(ell)
     return o, lse

@@ -72,18 +72,18 @@ MUTANTS = [
      "ok = allowed_mask(np.arange(rows), nq, nk, causal, k_len_b,"),
     # --- tile recurrence and merge ------------------------------------------
     ("rescale_l_only", "online.py",
-     "u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]", "u[r] = u[r] + e @ v[ka:kb][ok[r]]"),
+     "alpha_a * u_a + alpha_b * u_b", "u_a + alpha_b * u_b"),
     ("rescale_u_only", "online.py",
-     "ell[r] = alpha * ell[r] + e.sum()", "ell[r] = ell[r] + e.sum()"),
+     "alpha_a * l_a + alpha_b * l_b", "l_a + alpha_b * l_b"),
     ("alpha_inverted", "online.py",
-     "alpha = np.exp(m[r] - m_new) if ell[r] > 0 else 0.0",
-     "alpha = np.exp(m_new - m[r]) if ell[r] > 0 else 0.0"),
-    ("tile_local_softmax_sum", "online.py",
-     "u[r] = alpha * u[r] + e @ v[ka:kb][ok[r]]",
-     "u[r] = u[r] + (e @ v[ka:kb][ok[r]]) / e.sum() * ell[r]"),
+     "alpha_a = np.exp(m_a - m)", "alpha_a = np.exp(m - m_a)"),
+    ("merge_without_rebase", "online.py",
+     "states[r] = merge_states(old, block_state(s[r, ok[r]], v[ka:kb][ok[r]]))",
+     "blk = block_state(s[r, ok[r]], v[ka:kb][ok[r]])\n"
+     "                states[r] = blk if old is None else (max(old[0], blk[0]), old[1] + blk[1], old[2] + blk[2])"),
     ("tile_local_positions", "online.py",
-     "ok = allowed_mask(np.arange(qa, qb), nq, nk, causal,\n                              k_len_b)[:, ka:kb]",
-     "ok = allowed_mask(np.arange(qb - qa), qb - qa, kb - ka, causal,\n                              k_len_b)"),
+     "ok = allowed_mask(np.arange(qa, qb), nq, nk, causal, k_len_b)[:, ka:kb]",
+     "ok = allowed_mask(np.arange(qb - qa), qb - qa, kb - ka, causal, k_len_b)"),
     ("bias_tile_misaligned", "online.py",
      "s = s + np.asarray(bias, dtype=np.float64)[qa:qb, ka:kb]",
      "s = s + np.asarray(bias, dtype=np.float64)[qa:qb, :kb - ka]"),
@@ -92,8 +92,7 @@ MUTANTS = [
     ("duplicates_allowed", "online.py",
      "if np.any(seen != 1):", "if np.any(seen < 1):"),
     ("lse_drops_max_online", "online.py",
-     "lse[qa:qb][nonempty] = m[nonempty] + np.log(ell[nonempty])",
-     "lse[qa:qb][nonempty] = np.log(ell[nonempty])"),
+     "lse[qa + r] = m + np.log(ell)", "lse[qa + r] = np.log(ell)"),
     ("merge_rescale_dropped", "online.py",
      "return m, alpha_a * l_a + alpha_b * l_b, alpha_a * u_a + alpha_b * u_b",
      "return m, alpha_a * l_a + alpha_b * l_b, u_a + u_b"),
