@@ -407,16 +407,6 @@ struct FwdTile {
     }
     f32x4 s[4][2];
     qk_tile<DK, DV>(s, qf, kcur, la);
-    int row_lo[2] = {0, 0};
-    unsigned row_span[2] = {0u, 0u};
-    if (MASK) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int lo = key_lo(mr, qrow0 + 16 * qb), end = key_end(mr, qrow0 + 16 * qb, klen);
-        row_lo[qb] = lo;
-        row_span[qb] = end > lo ? (unsigned)(end - lo) : 0u;
-      }
-    }
     Philox4 zw[2];
     if (DROP) {
 #pragma unroll
@@ -424,8 +414,30 @@ struct FwdTile {
     }
     bf16x8 pb[2][2];
     float alpha[2];
-    const bool grow = softmax_tile<MASK, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
-                                                     vec_bias != 0, g, zw, dsp.keep);
+    int row_lo[2] = {0, 0};
+    unsigned row_span[2] = {0u, 0u};
+    bool grow;
+    // A tile that needs the mask for some row of the work-group may still
+    // lie inside every range of this wave's rows (the wave's 32 rows span
+    // 32 positions, the work-group's 128): then this wave takes it unmasked.
+    // Its last row has the largest lowest key, its first row the smallest
+    // end.
+    if (MASK && __builtin_amdgcn_readfirstlane(
+                    (int)(key_lo(mr, wlast) <= n0 && key_end(mr, wfirst, klen) >= n0 + kBN))) {
+      grow = softmax_tile<false, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
+                                             vec_bias != 0, g, zw, dsp.keep);
+    } else {
+      if (MASK) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int lo = key_lo(mr, qrow0 + 16 * qb), end = key_end(mr, qrow0 + 16 * qb, klen);
+          row_lo[qb] = lo;
+          row_span[qb] = end > lo ? (unsigned)(end - lo) : 0u;
+        }
+      }
+      grow = softmax_tile<MASK, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
+                                            vec_bias != 0, g, zw, dsp.keep);
+    }
     if (grow) {
 #pragma unroll
       for (int d = 0; d < DV / 16; ++d) {
