@@ -82,12 +82,13 @@ KERNEL_SOURCES = {
     "dropout_bwd": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
                     "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h",
                     "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
-    "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h"],
+    "decode": ["online_softmax_05_amd/csrc/fa_decode.hip", "online_softmax_05_amd/csrc/fa_common.h",
+               "online_softmax_05_amd/csrc/fa_merge.h"],
     "backward": ["online_softmax_05_amd/csrc/fa_bwd.hip", "online_softmax_05_amd/csrc/fa_bwd_bf16.hip",
                  "online_softmax_05_amd/csrc/fa_tiles.h", "online_softmax_05_amd/csrc/fa_common.h",
                  "online_softmax_05_amd/csrc/fa_mask.h", "online_softmax_05_amd/csrc/fa_dropout.h"],
     "decode_mq": ["online_softmax_05_amd/csrc/fa_decode_mq.hip", "online_softmax_05_amd/csrc/fa_tiles.h",
-                  "online_softmax_05_amd/csrc/fa_common.h"],
+                  "online_softmax_05_amd/csrc/fa_common.h", "online_softmax_05_amd/csrc/fa_merge.h"],
 }
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false>",
                 "long": "fwd_bf16_fast_kernel<128, 128, false, false>",

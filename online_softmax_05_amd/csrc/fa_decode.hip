@@ -27,6 +27,7 @@
 // Logits are carried in the base-2 domain (t = s * log2 e), so m_c is a
 // base-2 maximum and lse = ln2 * (m + log2 l).
 #include "fa_common.h"
+#include "fa_merge.h"
 #include "launch.h"
 
 namespace fa {
@@ -191,23 +192,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
                                                           int max_chunks) {
   const int bhi = blockIdx.x;
   const int b = bhi / H;
-  const int lane = threadIdx.x;
   const int klen = clamp_klen(k_len, b, Nk);
   const int n_c = (klen + chunk - 1) / chunk;
   const size_t base = (size_t)bhi * max_chunks;
-  float m = kNegInf;
-  for (int c = 0; c < n_c; ++c) m = fmaxf(m, ws_ml[(base + c) * 2]);
-  float l = 0.f;
-  for (int c = 0; c < n_c; ++c) l = fmaf(fast_exp2(ws_ml[(base + c) * 2] - m), ws_ml[(base + c) * 2 + 1], l);
-  const bool nonempty = n_c > 0 && l > 0.f;
-  const float inv = nonempty ? 1.f / l : 0.f;
-  T* orow = o + (size_t)bhi * dv;
-  for (int d = lane; d < dv; d += 64) {
-    float u = 0.f;
-    for (int c = 0; c < n_c; ++c) u = fmaf(fast_exp2(ws_ml[(base + c) * 2] - m), ws_u[(base + c) * dv + d], u);
-    orow[d] = Elem<T>::store(u * inv);
-  }
-  if (lse != nullptr && lane == 0) lse[bhi] = nonempty ? (m + fast_log2(l)) * kLn2 : kNegInf;
+  merge_chunk_states(ws_u + base * dv, (size_t)dv, ws_ml + base * 2, 2, n_c, dv, o + (size_t)bhi * dv,
+                     lse != nullptr ? lse + bhi : nullptr, [](float x) { return Elem<T>::store(x); });
 }
 
 // ---------------------------------------------------------------------------

@@ -32,6 +32,7 @@
 // by its definition -- logits to LDS, chunk maximum, then exponentials and
 // the weighted value sum -- one row after another.
 #include "fa_common.h"
+#include "fa_merge.h"
 #include "fa_tiles.h"
 #include "launch.h"
 
@@ -333,29 +334,11 @@ __global__ __launch_bounds__(64) void mq_merge_kernel(const float* __restrict__ 
   const int i = (int)(row % Nq);
   const size_t bh = row / Nq;
   const int b = (int)(bh / H);
-  const int lane = threadIdx.x;
   const int klen = clamp_klen(k_len, b, Nk);
   const int n_c = (klen + chunk - 1) / chunk;
-  float m = kNegInf;
-  for (int c = 0; c < n_c; ++c) m = fmaxf(m, ws_ml[state_index(bh, c, i, max_chunks, Nq) * 2]);
-  const float mu = (m == kNegInf) ? 0.f : m;
-  float l = 0.f;
-  for (int c = 0; c < n_c; ++c) {
-    const size_t si = state_index(bh, c, i, max_chunks, Nq);
-    l = fmaf(fast_exp2(ws_ml[si * 2] - mu), ws_ml[si * 2 + 1], l);
-  }
-  const bool nonempty = l > 0.f;
-  const float inv = nonempty ? 1.f / l : 0.f;
-  T* orow = o + row * dv;
-  for (int d = lane; d < dv; d += 64) {
-    float u = 0.f;
-    for (int c = 0; c < n_c; ++c) {
-      const size_t si = state_index(bh, c, i, max_chunks, Nq);
-      u = fmaf(fast_exp2(ws_ml[si * 2] - mu), ws_u[si * dv + d], u);
-    }
-    orow[d] = store_elem<T>(u * inv);
-  }
-  if (lse != nullptr && lane == 0) lse[row] = nonempty ? (m + fast_log2(l)) * kLn2 : kNegInf;
+  const size_t s0 = state_index(bh, 0, i, max_chunks, Nq);  // chunk c: s0 + c * Nq
+  merge_chunk_states(ws_u + s0 * dv, (size_t)Nq * dv, ws_ml + s0 * 2, (size_t)Nq * 2, n_c, dv, o + row * dv,
+                     lse != nullptr ? lse + row : nullptr, [](float x) { return store_elem<T>(x); });
 }
 
 template <typename T>

@@ -55,6 +55,8 @@ CASES = [
     (2, 2, 7, 333, 128, 128, False, 64),
     (2, 2, 5, 500, 64, 64, True, 128),      # general path
     (1, 3, 3, 200, 40, 24, True, 64),
+    (2, 2, 3, 8400, 128, 128, True, 64),    # more than 64 chunks per row (the merge's chunk groups)
+    (2, 1, 2, 4300, 64, 24, False, 64),
 ]
 
 

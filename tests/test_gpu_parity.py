@@ -394,6 +394,29 @@ def test_decode_fast_path_lengths(dev, chunk):
     compare(o[:, :, None], lse[:, :, None], o_ref, lse_ref, torch.bfloat16, f"decode fast chunk={chunk}")
 
 
+@pytest.mark.parametrize("dt,dims", [("bf16", (128, 128)), ("f32", (64, 24)), ("bf16", (40, 1))])
+def test_decode_many_chunks(dev, dt, dims):
+    """More than 64 chunk states per row (the merge takes them 64 at a time)
+    and head dims below the wave width."""
+    import online_softmax_05_amd as fa
+
+    dk, dv = dims
+    g = torch.Generator().manual_seed(4000 + dk + dv)
+    lens = [4095, 4096, 4097, 4160, 8191]
+    B, H, Nk = len(lens), 2, 8191
+    q = torch.randn(B, H, dk, generator=g).to(DT[dt])
+    k = torch.randn(B, H, Nk, dk, generator=g).to(DT[dt])
+    v = torch.randn(B, H, Nk, dv, generator=g).to(DT[dt])
+    k_len = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(dk)
+    say(f"decode many chunks {dt} dims={dims}")
+    o, lse = fa.fa_decode_splitk(q.to(dev), k.to(dev), v.to(dev), k_len.to(dev), scale=scale, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(f64(q)[:, :, None], f64(k), f64(v), scale=scale32(scale),
+                                          k_len=k_len.numpy())
+    compare(o[:, :, None], lse[:, :, None], o_ref, lse_ref, DT[dt], f"decode many chunks {dt} dims={dims}")
+
+
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (40, 24), (1, 1)])
 def test_decode_matches_fwd_nq1(dev, dims):
     """Decode equals the prefill kernel with one query row (causal is a no-op
