@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_fast_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations stay scalar
   const int r16 = lane & 15, g = lane >> 4;
 
   const TileCoord tc = fwd_tile(blockIdx.x, gridDim.x, fm, mr.wr >= 0);
