@@ -208,6 +208,18 @@ def launch_fields(t):
 # CPU baseline (the oracle, on a bounded sample)
 # ---------------------------------------------------------------------------
 
+def blas_name():
+    """The BLAS library numpy calls (threadpoolctl's view), e.g. "openblas 0.3.27"."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library threadpoolctl looks for)
+        from threadpoolctl import threadpool_info
+
+        libs = [f"{d.get('internal_api')} {d.get('version')}" for d in threadpool_info() if d.get("user_api") == "blas"]
+        return ", ".join(libs) if libs else None
+    except Exception:  # noqa: BLE001
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -270,7 +282,7 @@ def cpu_baseline_prefill(inp, name, budget_s, out, lse):
         heads += 1
         if elapsed >= budget_s:
             break
-    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), blas=blas_name(), kind="oracle",
                 sample=f"{heads} of {B * H} heads of the {name} workload, every query row, dense float64 "
                        f"numpy oracle, {elapsed:.1f} s of oracle time (input copies excluded)",
                 seconds=elapsed, cpu=cpu_model()), err
@@ -306,7 +318,7 @@ def cpu_baseline_decode(inp, budget_s, out, lse, nq=1, name="decode"):
             pairs += 1
         if elapsed >= budget_s:
             break
-    return dict(value=nbytes / elapsed / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle",
+    return dict(value=nbytes / elapsed / 1e9, unit="GB/s", cores=blas_threads(), blas=blas_name(), kind="oracle",
                 sample=f"{pairs} of {B * H} (sequence, head) pairs ({nq} query row{'s' if nq > 1 else ''} each) of "
                        f"the {name} workload, dense float64 numpy oracle, {elapsed:.1f} s of oracle time "
                        f"(input copies excluded)",
@@ -403,7 +415,7 @@ def cpu_baseline_backward(inp, budget_s, grads, name="backward"):
         heads += 1
         if elapsed >= budget_s:
             break
-    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), blas=blas_name(), kind="oracle",
                 sample=f"{heads} of {B * H} heads of the {name} workload, dense float64 numpy oracle "
                        f"(forward included), {elapsed:.1f} s of oracle time (input copies excluded)",
                 seconds=elapsed, cpu=cpu_model()), dict(err, heads_compared=heads, kind="max abs / max |ref|")
@@ -615,7 +627,7 @@ def run_small(name, args, dev):
             o_ref, l_ref = oracle.attention_ref(*args64, scale=scale, causal=inp["causal"], k_len=kl, bias=bias64)
             elapsed += time.perf_counter() - ts
             reps += 1
-        res["cpu_baseline"] = dict(value=reps * flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(),
+        res["cpu_baseline"] = dict(value=reps * flops / elapsed / 1e12, unit="TFLOP/s", cores=blas_threads(), blas=blas_name(),
                                    kind="oracle", sample=f"the whole {name} workload, {reps} runs of the dense "
                                                          f"float64 numpy oracle, {elapsed:.2f} s",
                                    seconds=elapsed, cpu=cpu_model())
