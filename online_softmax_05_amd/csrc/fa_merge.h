@@ -35,12 +35,17 @@ __device__ __forceinline__ void merge_chunk_states(const float* __restrict__ u, 
                                                    const float* __restrict__ ml, size_t s_ml, int n_c, int dv,
                                                    T* __restrict__ orow, float* __restrict__ lse_out, Store store) {
   const int lane = threadIdx.x & 63;
-  float mx = kNegInf;
-  for (int c = lane; c < n_c; c += 64) mx = fmaxf(mx, ml[c * s_ml]);
+  // each lane's first chunk state, read once (most rows have at most 64
+  // chunks; more are read again in the passes below)
+  const float m0 = lane < n_c ? ml[lane * s_ml] : kNegInf;
+  const float l0 = lane < n_c ? ml[lane * s_ml + 1] : 0.f;
+  float mx = m0;
+  for (int c = lane + 64; c < n_c; c += 64) mx = fmaxf(mx, ml[c * s_ml]);
   mx = wave_max64(mx);
   const float mu = (mx == kNegInf) ? 0.f : mx;
-  float ls = 0.f;
-  for (int c = lane; c < n_c; c += 64) ls = fmaf(fast_exp2(ml[c * s_ml] - mu), ml[c * s_ml + 1], ls);
+  const float w0 = fast_exp2(m0 - mu);  // weight of chunk `lane` (0 past n_c)
+  float ls = w0 * l0;
+  for (int c = lane + 64; c < n_c; c += 64) ls = fmaf(fast_exp2(ml[c * s_ml] - mu), ml[c * s_ml + 1], ls);
   const float l = wave_sum64(ls);
   const bool nonempty = l > 0.f;
   const float inv = nonempty ? 1.f / l : 0.f;
@@ -52,7 +57,8 @@ __device__ __forceinline__ void merge_chunk_states(const float* __restrict__ u, 
     float acc = 0.f;
     for (int c0 = 0; c0 < n_c; c0 += 64) {
       const int cl = c0 + lane;
-      const int wl = __float_as_int(cl < n_c ? fast_exp2(ml[cl * s_ml] - mu) : 0.f);  // weight of chunk c0 + lane
+      const float wf = c0 == 0 ? w0 : (cl < n_c ? fast_exp2(ml[cl * s_ml] - mu) : 0.f);
+      const int wl = __float_as_int(wf);  // weight of chunk c0 + lane
       const int cn = min(64, n_c - c0);
       const float* uc = u + (size_t)c0 * s_u + (act ? d : 0);
       int j = 0;
