@@ -142,6 +142,15 @@ def stored_traffic(name):
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
+def traffic_source(name):
+    """Where roofline.traffic comes from: it is not measured in this run."""
+    if stored_traffic(name) is None:
+        return None
+    return (f"profiles/{name}_traffic.json: FETCH_SIZE + WRITE_SIZE of separate rocprofv3 --pmc runs of this "
+            f"workload, scaled by a plain copy's readings; used because the kernel sources still hash to the "
+            f"value recorded with it")
+
+
 def clock_fields(name, achieved_tflops):
     """Measured shader clock and MFMA busy fraction from the stored counter
     record, and the fraction of the dense bf16 peak at that clock."""
@@ -368,7 +377,7 @@ def run_prefill(name, args, dev):
         workload=workloads.DESCRIPTIONS[name], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_BF16_TFLOPS,
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic, traffic_source=traffic_source(name),
                       kernel=KERNEL_NAMES[name], **launch_fields(t), **clock_fields(name, achieved),
                       algorithmic_flops_per_launch=flops,
                       algorithmic_bytes_per_launch=2 * B * H * N * (2 * dk + dv) + 2 * B * H * N * dv
@@ -454,7 +463,7 @@ def run_backward(args, dev, name="backward"):
         workload=workloads.DESCRIPTIONS[name], value=value, unit="TFLOP/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_BF16_TFLOPS,
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=stored_traffic(name),
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=stored_traffic(name), traffic_source=traffic_source(name),
                       kernel=KERNEL_NAMES[name], **launch_fields(t), **clock_fields(name, achieved),
                       algorithmic_flops_per_launch=flops),
         config=dict(workload=workloads.DESCRIPTIONS[name], B=B, H=H, Nq=N, Nk=N, dk=dk, dv=dv, causal=True,
@@ -499,7 +508,7 @@ def run_decode_mq(args, dev):
         workload=workloads.DESCRIPTIONS["decode_mq"], value=value, unit="GB/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
-                      traffic=stored_traffic("decode_mq"), kernel=KERNEL_NAMES["decode_mq"], **launch_fields(t),
+                      traffic=stored_traffic("decode_mq"), traffic_source=traffic_source("decode_mq"), kernel=KERNEL_NAMES["decode_mq"], **launch_fields(t),
                       algorithmic_bytes_per_launch=nbytes),
         config=dict(workload=workloads.DESCRIPTIONS["decode_mq"], B=B, H=H, Nq=Nq, Nk_max=Nk, dk=dk, dv=dv,
                     chunk=chunk, causal=True, dtype="bf16", k_len_sum=int(kl.sum().item())),
@@ -543,7 +552,7 @@ def run_decode(args, dev):
         workload=workloads.DESCRIPTIONS["decode"], value=value, unit="GB/s", ms_per_step=t["ms_per_step"],
         frac_of_peak=value / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
-                      traffic=stored_traffic("decode"), kernel=KERNEL_NAMES["decode"], **launch_fields(t),
+                      traffic=stored_traffic("decode"), traffic_source=traffic_source("decode"), kernel=KERNEL_NAMES["decode"], **launch_fields(t),
                       algorithmic_bytes_per_launch=nbytes),
         config=dict(workload=workloads.DESCRIPTIONS["decode"], B=B, H=H, Nk_max=Nk, dk=dk, dv=dv, chunk=chunk,
                     dtype="bf16", k_len_sum=int(kl.sum().item())),
