@@ -248,7 +248,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       Philox4 zw;
-      if (DROP) zw = dropout_words(dsp, row[qb], t, (uint32_t)bh, g);
+      // plain xors here: with the fused form the d = 128 dropout instance
+      // spills 16 registers
+      if (DROP) zw = dropout_words<false>(dsp, row[qb], t, (uint32_t)bh, g);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int key0 = j0 + 16 * kb + 4 * g;

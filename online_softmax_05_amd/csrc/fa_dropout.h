@@ -27,6 +27,10 @@ struct Philox4 {
   uint32_t x[4];
 };
 
+// BITOP3: each round's two three-way xors as one v_bitop3_b32 each (fewer
+// instructions); false keeps two v_xor_b32 each, which a kernel at its
+// register limit may schedule with fewer live values.
+template <bool BITOP3 = true>
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                  uint32_t k1) {
   constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
@@ -35,8 +39,14 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   for (int r = 0; r < 10; ++r) {
     const uint64_t pa = (uint64_t)kMulA * c0;  // one v_mad_u64_u32 each
     const uint64_t pb = (uint64_t)kMulB * c2;
-    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+    uint32_t n0, n2;
+    if (BITOP3) {  // truth table 0x96: a ^ b ^ c
+      n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c1, k0, 0x96);
+      n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c3, k1, 0x96);
+    } else {
+      n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
+      n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+    }
     c1 = (uint32_t)pb;
     c3 = (uint32_t)pa;
     c0 = n0;
@@ -59,8 +69,9 @@ struct DropoutSpec {
 };
 
 // The four random words of (row i, 64-key tile t, group g) of head bh.
+template <bool BITOP3 = true>
 __device__ __forceinline__ Philox4 dropout_words(const DropoutSpec& d, int i, int t, uint32_t bh, int g) {
-  return philox4x32_10((uint32_t)i, (uint32_t)t, bh, (uint32_t)g, d.seed_lo, d.seed_hi);
+  return philox4x32_10<BITOP3>((uint32_t)i, (uint32_t)t, bh, (uint32_t)g, d.seed_lo, d.seed_hi);
 }
 
 // Word w (0..3, any runtime value) of a generator output, without indexing
