@@ -41,7 +41,8 @@ roofline.traffic comes from a stored rocprofv3 counter summary
 mfma_busy from another (profiles/<workload>_counters.json: GRBM_GUI_ACTIVE per
 XCD over the dispatch duration, SQ_VALU_MFMA_BUSY_CYCLES over
 GRBM_GUI_ACTIVE x 1024 SIMDs); each is reported only while the kernel
-sources still hash to the value recorded with it.  frac_at_clock is achieved
+sources (their code: comments and whitespace are not hashed) still hash to
+the value recorded with it.  frac_at_clock is achieved
 over the dense peak at that measured clock (256 CU x 4096 FLOP/clk x clock).
 
 cpu_baseline times the float64 oracle (test infrastructure, used here only
@@ -108,10 +109,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace runs collapsed, so
+    that a stored record stays tied to the code, not to its comments."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":  # string or character literal: copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(name):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[name]:
-        h.update((ROOT / rel).read_bytes())
+        h.update(_code_only((ROOT / rel).read_text()).encode())
     return h.hexdigest()[:16]
 
 

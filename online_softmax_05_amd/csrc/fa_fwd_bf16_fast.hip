@@ -34,12 +34,14 @@
 //   read, so V stays in its natural row-major order.
 // * Row sums of P are taken in fp32 before P is rounded to bf16 (a sum of
 //   the rounded values on the matrix cores would leave ~1e-3 relative
-//   error in l, and so in lse, on rows dominated by a few keys).
+//   error in l, and so in lse, on rows dominated by a few keys); O is
+//   divided by a second fp32 sum, of the rounded weights that multiply V.
 // * Double buffering: the loads of tile t+1 are in flight during the whole
 //   of tile t, and one barrier per tile publishes them.  Two work-groups
-//   share each CU, so one wave's softmax (VALU) overlaps the other wave's
-//   matrix products on the same SIMD.  Tiles that need no mask for any row
-//   of the work-group run a variant without mask code.
+//   share each CU, so one wave's softmax (VALU) can overlap the other
+//   wave's matrix products on the same SIMD.  Tiles that need no mask for
+//   any row of the work-group run a variant without mask code, and so does
+//   a wave whose 32 rows all see the whole of a masked tile.
 // * Position masks (causal in either alignment, sliding windows) arrive as a
 //   visible key range [lo, end) per row, both ends growing with the row
 //   ([GS] section 6).  A work-group visits the key tiles that meet the union
