@@ -95,6 +95,36 @@ def test_fwd_ex_sweep(dev, c):
         assert e_o <= tol["o"] * r and e_l <= tol["lse"], (e_o, e_l)
 
 
+def _fast_cases(n, seed):
+    """Cases the fast bf16 kernel takes (head dims 64/128, default tile
+    width), several query tiles of 128 rows and ragged lengths, so that
+    masked edge tiles, tiles that one wave sees whole while another does not,
+    and unmasked runs all occur."""
+    rng = np.random.default_rng(seed)
+    dims = [(128, 128), (64, 64), (128, 64), (64, 128)]
+    out = []
+    for i in range(n):
+        dk, dv = dims[int(rng.integers(0, len(dims)))]
+        out.append(dict(
+            i=100 + i, B=1, H=int(rng.integers(1, 3)), nq=int(rng.choice([300, 511, 700, 1000])),
+            nk=int(rng.choice([256, 513, 800, 1000])), dk=dk, dv=dv, dt="bf16", causal=bool(rng.integers(0, 2)),
+            align=["bottom_right", "top_left"][int(rng.integers(0, 2))],
+            wl=[None, None, 31, 100, 257][int(rng.integers(0, 5))],
+            wr=[None, None, None, 0, 33][int(rng.integers(0, 5))],
+            keep=[256, 256, 230][int(rng.integers(0, 3))],
+            bias=bool(rng.integers(0, 2)), kl=[None, "random"][int(rng.integers(0, 2))],
+            bn=[0, 64][int(rng.integers(0, 2))], seed=int(rng.integers(0, 2**63))))
+    return out
+
+
+FWD_FAST = _fast_cases(16, 77)
+
+
+@pytest.mark.parametrize("c", FWD_FAST, ids=lambda c: f"fast{c['i']}")
+def test_fwd_ex_sweep_fast_kernel(dev, c):
+    test_fwd_ex_sweep(dev, c)
+
+
 BWD = _cases(24, 4052)
 
 
