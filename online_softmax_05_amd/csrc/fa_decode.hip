@@ -265,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_fast_kernel(
   constexpr int D = kFastD;
   __shared__ float red_u[4][D];
   __shared__ float red_ml[4][2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // uniform: the buffer descriptors below stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = blockIdx.x / BH;
   const int bhi = blockIdx.x - c * BH;
   const int b = bhi / H;
@@ -277,13 +278,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial_fast_kernel(
   const size_t bh = (size_t)bhi;
   const int col = lane & 15, grp = lane >> 4;  // 16-byte column of a row; row group
   const u32x4 qf = *reinterpret_cast<const u32x4*>(q + bh * D + col * 8);
-  const uint16_t* kp = k + (bh * Nk + c0) * D + col * 8;
-  const uint16_t* vp = v + (bh * Nk + c0) * D + col * 8;
 
   // rows of this wave: one quarter of the chunk (a multiple of 16 rows)
   const int quarter = chunk / 4;
   const int r_begin = wave * quarter;
   const int r_end = min(r_begin + quarter, len);
+  // This wave's rows of K and V as buffers of r_end - r_begin rows: a load
+  // at or past r_end fails the hardware range check and returns zeros, so
+  // the loads need no branch (rows of other waves and rows at or past the
+  // key length are never read).  Cache policy 2 = nontemporal: every cache
+  // row is read once per call.
+  const uint32_t bytes = (uint32_t)max(r_end - r_begin, 0) * D * 2;
+  const size_t first = (bh * Nk + c0 + r_begin) * D;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + first), (short)0, (int)bytes, 0x00020000);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + first), (short)0, (int)bytes, 0x00020000);
+  const uint32_t lane_off = (uint32_t)(grp * D * 2 + col * 16);
 
   DecState st;
   st.m = kNegInf;
@@ -291,48 +300,52 @@ __global__ __launch_bounds__(kThreads) void decode_partial_fast_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.u[e] = 0.f;
 
-#pragma unroll 2
-  for (int r0 = r_begin; r0 < r_end; r0 += 16) {
-    u32x4 kv[4], vv[4];
+  // kSteps 16-row steps per iteration: their 8 * kSteps loads are issued
+  // together, so each wave keeps that many in flight (measured on the
+  // decode workload: 4 steps 1.2% faster than 1 step of guarded loads)
+  constexpr int kSteps = 4;
+  for (int r00 = r_begin; r00 < r_end; r00 += 16 * kSteps) {
+    u32x4 kv[kSteps][4], vv[kSteps][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * i + grp;
-      const bool ok = row < r_end;
-      // nontemporal: every cache row is read once per call (measured:
-      // 5.8 -> 6.5 TB/s on the decode workload)
-      kv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)row * D))
-                 : u32x4{0u, 0u, 0u, 0u};
-      vv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)row * D))
-                 : u32x4{0u, 0u, 0u, 0u};
-    }
-    float sc[4];
-    float mx = kNegInf;
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float d = row16_sum(dot8_bf16(kv[i], qf));
-      sc[i] = (r0 + 4 * i + grp < r_end) ? d * scale_log2 : kNegInf;
-      mx = fmaxf(mx, sc[i]);
-    }
-    const float m_new = fmaxf(st.m, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(st.m - m_use);
-    st.m = m_new;
-    float psum = 0.f;
-    float p[4];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)(r00 - r_begin + 16 * s + 4 * i) * (D * 2) + lane_off;
+        kv[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 2);
+        vv[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 2);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(sc[i] - m_use);
-      psum += p[i];
-    }
-    st.l = fmaf(alpha, st.l, psum);
+    for (int s = 0; s < kSteps; ++s) {
+      const int r0 = r00 + 16 * s;
+      float sc[4];
+      float mx = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.u[e] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        const float d = row16_sum(dot8_bf16(kv[s][i], qf));
+        sc[i] = (r0 + 4 * i + grp < r_end) ? d * scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[i]);
+      }
+      const float m_new = fmaxf(st.m, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(st.m - m_use);
+      st.m = m_new;
+      float psum = 0.f;
+      float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(sc[i] - m_use);
+        psum += p[i];
+      }
+      st.l = fmaf(alpha, st.l, psum);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        st.u[2 * w] = fmaf(p[i], bf16_lo(vv[i][w]), st.u[2 * w]);
-        st.u[2 * w + 1] = fmaf(p[i], bf16_hi(vv[i][w]), st.u[2 * w + 1]);
+      for (int e = 0; e < 8; ++e) st.u[e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          st.u[2 * w] = fmaf(p[i], bf16_lo(vv[s][i][w]), st.u[2 * w]);
+          st.u[2 * w + 1] = fmaf(p[i], bf16_hi(vv[s][i][w]), st.u[2 * w + 1]);
+        }
       }
     }
   }
