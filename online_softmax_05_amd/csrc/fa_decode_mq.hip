@@ -17,16 +17,19 @@
 // the merge skips; a row with no allowed key at all gets o = 0, lse = -inf
 // ([GS] section 6).
 //
-// Matrix-core path (bf16, dk = dv = 128; tiles loaded nontemporal, since
-// each cache row is read once per call: 5.3 -> 5.9 TB/s measured): the
-// chunk's K and V stream through
-// LDS in 64-key tiles; wave w owns keys 16w .. 16w+15 of every tile for all
-// rows.  S^T = K Q^T comes from v_mfma_f32_16x16x32_bf16 (a lane holds 4 keys
-// of one row), each wave keeps an online state per row over its keys ([GS]
-// section 5), and O^T += V^T P^T uses v_mfma_f32_16x16x16_bf16, whose B
-// operand layout is exactly the S^T accumulator's (4 keys of one row per
-// lane), so P^T needs no data movement; V^T comes from ds_read_b64_tr_b16.
-// The four waves' states are merged at the end of the chunk.
+// Matrix-core path (bf16, dk = dv = 128): wave w owns keys 16w .. 16w+15 of
+// every 64-key tile of the chunk, for all rows, and runs its own pipeline
+// with two tiles in flight ahead of the one it consumes.  Its K rows go
+// straight into registers in the A-operand layout of S^T = K Q^T
+// (v_mfma_f32_16x16x32_bf16; a lane then holds 4 keys of one row); its V rows
+// go into its own rows of a three-slot LDS ring, since O^T += V^T P^T
+// (v_mfma_f32_16x16x16_bf16, whose B operand layout is exactly the S^T
+// accumulator's, so P^T needs no data movement) wants V^T, which
+// ds_read_b64_tr_b16 gives.  No wave reads another's rows, so the waves meet
+// only at the end of the chunk, where their online states ([GS] section 5)
+// are merged.  V is loaded nontemporal (each cache row is read once per
+// call); K is not: its loads read 64 of a row's 256 bytes each, and the
+// nontemporal form of those measured slower.
 //
 // General path (fp32 inputs, other head dims): the chunk state of each row
 // by its definition -- logits to LDS, chunk maximum, then exponentials and
@@ -40,7 +43,6 @@ namespace fa {
 namespace {
 
 using tiles::cvt_pk_bf16;
-using tiles::frag_read;
 using tiles::HeadBuf;
 using tiles::head_buf;
 using tiles::kTile;
@@ -160,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void mq_partial_general_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kD = 128;
+constexpr int kStages = 3;  // V ring slots: two tiles in flight ahead of the consumed one
 
 // max / sum over the four lanes q, q+16, q+32, q+48 that share a row
 __device__ __forceinline__ float quad_max(float x) {
@@ -175,24 +178,25 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
+template <int S>
+__global__ __launch_bounds__(kThreads, 3) void mq_partial_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ k_len, float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int BH, int Nq,
     int Nk, int chunk, int max_chunks, float scale_log2, int causal) {
   constexpr int ROW = Tile<kD>::ROW;
-  // K and V tiles, double buffered in separate arrays selected at compile
-  // time (the loop below is unrolled by two); K0 and V0 hold the
-  // end-of-chunk merge afterwards
-  __shared__ __attribute__((aligned(1024))) char kb0[Tile<kD>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[Tile<kD>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[Tile<kD>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[Tile<kD>::BYTES];
+  static_assert(S >= 2 && S <= 4, "the end-of-chunk merge uses two ring buffers; four slots at most");
+  // V ring of S tile buffers; wave w only ever writes and reads rows
+  // 16w .. 16w+15 of each, so the waves run their pipelines independently.
+  // Separate arrays, not one indexed array: the compiler then knows that a
+  // read of one slot does not wait for the direct loads into another.
+  __shared__ __attribute__((aligned(1024))) char vr0[Tile<kD>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vr1[Tile<kD>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vr2[S > 2 ? Tile<kD>::BYTES : 1];
+  __shared__ __attribute__((aligned(1024))) char vr3[S > 3 ? Tile<kD>::BYTES : 1];
+  const auto vring = [&](int s) -> lds_char* {
+    return (lds_char*)(s == 0 ? vr0 : s == 1 ? vr1 : s == 2 ? vr2 : vr3);
+  };
   __shared__ float red_ml[kWaves][kMaxRows][2];
-  lds_char* const K0 = (lds_char*)kb0;
-  lds_char* const K1 = (lds_char*)kb1;
-  lds_char* const V0 = (lds_char*)vb0;
-  lds_char* const V1 = (lds_char*)vb1;
-  static_assert(2 * kMaxRows * kD * 4 <= Tile<kD>::BYTES, "two waves' merge rows fit one tile buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,50 +209,52 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
   const int c0 = c * chunk;
   if (c0 >= klen) return;  // the merge reads only chunks below k_len
 
-  // this lane's row r16: its query as the B operand, its visible key end
   const bool rvalid = r16 < Nq;
   bf16x8 qf[kD / 32];
 #pragma unroll
   for (int t = 0; t < kD / 32; ++t)
     qf[t] = rvalid ? *reinterpret_cast<const bf16x8*>(q + (bh * Nq + r16) * kD + 32 * t + 8 * g) : bf16x8{};
   const int row_end = row_key_end(r16, Nq, klen, causal);
-  const int c_end = min(c0 + chunk, klen);  // last row (the largest end) sees all of them
+  const int c_end = min(c0 + chunk, klen);
   const int n_tiles = (c_end - c0 + kTile - 1) / kTile;
 
   TileAddr<kD> ta;
   ta.init(lane, wave);
-  // the buffers end at the sequence's key length: rows at or past k_len[b]
-  // fail the hardware range check and arrive as zeros, so the cache beyond
-  // the sequence is never read (whatever it holds, even NaN, cannot reach
-  // the P V products through a zero weight)
-  const HeadBuf kh = head_buf(k + bh * Nk * kD, (uint32_t)klen * kD * 2);
-  const HeadBuf vh = head_buf(v + bh * Nk * kD, (uint32_t)klen * kD * 2);
+  // the chunk's rows of K and V as buffers ending at c_end: loads past it
+  // fail the hardware range check and arrive as zeros without a memory
+  // access, so the pipeline below issues its loads unconditionally
+  const uint32_t cbytes = (uint32_t)(c_end - c0) * kD * 2;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (bh * Nk + c0) * kD), (short)0, (int)cbytes,
+                                                    0x00020000);
+  const HeadBuf vh = head_buf(v + (bh * Nk + c0) * kD, cbytes);
+  // K straight into registers in the A-operand layout of the S^T product:
+  // lane (r16, g) holds key 16 wave + r16, dims 32i + 8g .. +7 for k-step i
+  const uint32_t k_lane = (uint32_t)((16 * wave + r16) * ROW + 16 * g);
 
   float m = kNegInf, l = 0.f;  // this wave's state for row r16 (l: this lane's share)
   f32x4 o[kD / 16];            // O^T: dims 16db + 4g + j of row r16
 #pragma unroll
   for (int d = 0; d < kD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // key tile t (in kt, vt) while tile t + 1 loads into kn, vn
-  auto tile = [&](int t, const lds_char* kt, const lds_char* vt, lds_char* kn, lds_char* vn) {
-    wait_loads();
-    __syncthreads();
-    const int j0 = c0 + t * kTile;
-    if (t + 1 < n_tiles) {
-      load_tile<kD, tiles::kNonTemporal>(kh, j0 + kTile, ta.ld, kn, wave);
-      load_tile<kD, tiles::kNonTemporal>(vh, j0 + kTile, ta.ld, vn, wave);
-    }
-    // S^T for this wave's 16 keys: a lane holds keys 16 wave + 4g + j of row r16
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  u32x4 kr[S][kD / 32];
+  auto issue = [&](int t, u32x4 (&kx)[kD / 32], lds_char* vdst) {
 #pragma unroll
     for (int i = 0; i < kD / 32; ++i)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_read(kt + ta.frag[i] + 16 * wave * ROW), qf[i], s, 0, 0, 0);
-    const int key0 = j0 + 16 * wave + 4 * g;
+      kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)(t * kTile * ROW) + k_lane + 64 * i, 0, 0);
+    load_tile<kD, tiles::kNonTemporal>(vh, t * kTile, ta.ld, vdst, wave);
+  };
+  auto compute = [&](int t, const u32x4 (&kx)[kD / 32], const lds_char* vt) {
+    // S^T for this wave's 16 keys: a lane holds keys 16 wave + 4g + j of row r16
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kD / 32; ++i)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[i]), qf[i], sc, 0, 0, 0);
+    const int key0 = c0 + t * kTile + 16 * wave + 4 * g;
     float x[4];
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = (key0 + j < row_end) ? s[j] * scale_log2 : kNegInf;
+      x[j] = (key0 + j < row_end) ? sc[j] * scale_log2 : kNegInf;
       mx = fmaxf(mx, x[j]);
     }
     const float m_new = fmaxf(m, quad_max(mx));
@@ -269,19 +275,28 @@ __global__ __launch_bounds__(kThreads, 2) void mq_partial_bf16_kernel(
       o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[d], 0, 0, 0);
     }
   };
-  load_tile<kD, tiles::kNonTemporal>(kh, c0, ta.ld, K0, wave);
-  load_tile<kD, tiles::kNonTemporal>(vh, c0, ta.ld, V0, wave);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, K0, V0, K1, V1);
-    if (t + 1 < n_tiles) tile(t + 1, K1, V1, K0, V0);
+
+  // S - 1 tiles in flight ahead of the one being consumed; tile t uses ring
+  // slot t % S (the loop is unrolled by S so every slot is a compile-time
+  // address)
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s, kr[s], vring(s));
+  for (int t0 = 0; t0 < n_tiles; t0 += S) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int t = t0 + s;
+      if (t >= n_tiles) break;
+      issue(t + S - 1, kr[(s + S - 1) % S], vring((s + S - 1) % S));
+      compute(t, kr[s], vring(s));
+    }
   }
 
   // merge the four waves' states per row ([GS] section 4) through LDS
   l = quad_sum(l);
   wait_loads();
-  __syncthreads();  // tile buffers are free
-  // [wave][row][dim]: waves 0 and 1 in K0, waves 2 and 3 in V0
-  const auto red_u = [&](int w) { return (lds_float*)((w < 2 ? K0 : V0) + (w & 1) * kMaxRows * kD * 4); };
+  __syncthreads();  // ring buffers are free
+  // [wave][row][dim]: waves 0 and 1 in ring slot 0, waves 2 and 3 in slot 1
+  const auto red_u = [&](int w) { return (lds_float*)(vring(w >> 1) + (w & 1) * kMaxRows * kD * 4); };
   lds_float* const mine = red_u(wave);
 #pragma unroll
   for (int d = 0; d < kD / 16; ++d)
@@ -347,7 +362,7 @@ hipError_t launch_mq(const DecodeMqArgs& a, hipStream_t stream, bool mfma) {
   const long long n_part = (long long)BH * a.max_chunks;
   if (n_part > 0) {
     if (mfma)
-      hipLaunchKernelGGL(mq_partial_bf16_kernel, dim3((unsigned)n_part), dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL(mq_partial_bf16_kernel<kStages>, dim3((unsigned)n_part), dim3(kThreads), 0, stream,
                          (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.k_len, a.ws_u, a.ws_ml,
                          a.H, BH, a.Nq, a.Nk, a.chunk, a.max_chunks, a.scale * kLog2e, a.causal);
     else

@@ -57,6 +57,7 @@ CASES = [
     (1, 3, 3, 200, 40, 24, True, 64),
     (2, 2, 3, 8400, 128, 128, True, 64),    # more than 64 chunks per row (the merge's chunk groups)
     (2, 1, 2, 4300, 64, 24, False, 64),
+    (2, 2, 4, 4500, 128, 128, True, 2048),  # matrix-core path, the largest chunk, a ragged last chunk
 ]
 
 
@@ -102,7 +103,7 @@ def test_decode_mq_single_row_matches_decode(dev):
 
 def test_decode_mq_full_size_every_row(dev):
     """The multi-query decode workload (64x32 sequences x 4 causal rows, caches
-    of 8192 keys, lengths U{1..8192}, d128 bf16, 512-key chunks) in the launch
+    of 8192 keys, lengths U{1..8192}, d128 bf16, 2048-key chunks) in the launch
     configuration the benchmark times: every row of every (sequence, head)
     against the oracle over the cache truncated to the sequence's length."""
     import online_softmax_05_amd as fa
