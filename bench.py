@@ -91,10 +91,11 @@ KERNEL_SOURCES = {
     "decode_mq": ["online_softmax_05_amd/csrc/fa_decode_mq.hip", "online_softmax_05_amd/csrc/fa_tiles.h",
                   "online_softmax_05_amd/csrc/fa_common.h", "online_softmax_05_amd/csrc/fa_merge.h"],
 }
-KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false>",
-                "long": "fwd_bf16_fast_kernel<128, 128, false, false>",
-                "window": "fwd_bf16_fast_kernel<128, 128, false, false>",
-                "dropout": "fwd_bf16_fast_kernel<128, 128, false, true>",
+# (the fast forward's last template argument is its waves per work-group)
+KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
+                "long": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
+                "window": "fwd_bf16_fast_kernel<128, 128, false, false, 4>",
+                "dropout": "fwd_bf16_fast_kernel<128, 128, false, true, 4>",
                 "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true> + bwd_dkdv_bf16_kernel<128, 128, false, true>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
                 "backward": "bwd_dq_bf16_kernel<128, 128, false, false> + bwd_dkdv_bf16_kernel<128, 128, false, false>",
@@ -638,7 +639,7 @@ def run_small(name, args, dev):
         roof = dict(bound="mfma", achieved=flops / sec / 1e12, peak=mfma_peak, unit="TFLOP/s",
                     frac=flops / sec / 1e12 / mfma_peak)
     kern = {"small": "fwd_f32_kernel (fp32 matrix cores)", "masks_f32": "fwd_f32_kernel (fp32 matrix cores)",
-            "masks_bf16": "fwd_bf16_fast_kernel<128, 64, true, false>"}[name]
+            "masks_bf16": "fwd_bf16_fast_kernel<128, 64, true, false, 4>"}[name]
     res = dict(
         workload=workloads.DESCRIPTIONS[base] + ("" if base == "small" else f", {'bf16' if esz == 2 else 'fp32'}"),
         value=flops / (t["ms_per_step"] * 1e-3) / 1e12, unit="TFLOP/s", ms_per_step=t["ms_per_step"],

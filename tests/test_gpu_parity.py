@@ -245,6 +245,39 @@ def test_fast_kernel_odd_grids(dev, case):
     compare(o, lse, o_ref, lse_ref, torch.bfloat16, f"fast grid {case}")
 
 
+# (B, H, Nq, Nk, dk, dv, causal, align): launches the fast bf16 kernel runs
+# with eight waves (256 query rows) per work-group -- no left window, no
+# bias, no dropout and at least 512 such work-groups -- with ragged query
+# and key counts, random key lengths, both head dims and both causal
+# alignments (top-left through fa_fwd_ex)
+EIGHT_WAVE_CASES = [
+    (2, 256, 300, 300, 128, 128, True, None),      # 2 query tiles per head, the second ragged
+    (1, 512, 257, 400, 64, 128, False, None),      # one row past the first tile
+    (4, 128, 200, 520, 128, 64, True, None),       # 512 work-groups of 200 rows
+    (2, 256, 300, 260, 64, 64, True, "top_left"),  # Nq > Nk, top-left causal
+]
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"_{c[6]}_{c[7]}")
+def test_fast_kernel_eight_waves(dev, case):
+    import online_softmax_05_amd as fa
+
+    B, H, nq, nk, dk, dv, causal, align = case
+    inp = workloads.seeded_case(7100 + H + nq + dk, B, H, nq, nk, dk, dv, torch.bfloat16, causal=causal,
+                                k_len="random")
+    say(f"fast kernel, eight waves {case}")
+    d = workloads.to_device(inp, dev)
+    if align is None:
+        o, lse = fa.fa_fwd(d["q"], d["k"], d["v"], k_len=d["k_len"], scale=inp["scale"], causal=causal)
+    else:
+        o, lse = fa.fa_fwd_ex(d["q"], d["k"], d["v"], k_len=d["k_len"], scale=inp["scale"], causal=causal,
+                              align=align, window_left=None, window_right=None)
+        inp.update(align=align, window_left=None, window_right=None)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(inp)
+    compare(o, lse, o_ref, lse_ref, torch.bfloat16, f"eight waves {case}")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-3, 3.0])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_scale_values(dev, scale, dt):
