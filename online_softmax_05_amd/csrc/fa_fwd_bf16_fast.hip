@@ -35,7 +35,9 @@
 // * Row sums of P are taken in fp32 before P is rounded to bf16 (a sum of
 //   the rounded values on the matrix cores would leave ~1e-3 relative
 //   error in l, and so in lse, on rows dominated by a few keys); O is
-//   divided by a second fp32 sum, of the rounded weights that multiply V.
+//   divided by a second fp32 sum, of the rounded weights that multiply V
+//   (in eight-wave work-groups a product of P with a block of ones on the
+//   matrix cores, in four-wave ones v_dot2 against ones on the vector ALU).
 // * Double buffering: the loads of tile t+1 are in flight during the whole
 //   of tile t, and one barrier per tile publishes them.  Two waves share
 //   each SIMD (two 4-wave work-groups or one 8-wave work-group per CU), so
@@ -255,10 +257,21 @@ struct RowState {
 
 // O^T += V^T P^T for one tile: k-step kt covers keys 32kt .. 32kt+31, slot
 // s of lane group g holding key 32kt + 16(s/4) + 4g + s%4.
-template <int DK, int DV, int W>
-__device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&pb)[2][2], const lds_char* vt,
-                                        const LaneAddr<DK, DV, W>& la) {
+// With SUM, osum[qb] also accumulates the query block's sum of the rounded
+// weights, as products with a block of ones (every entry of the 16x16 result
+// is a query's sum).
+template <int DK, int DV, int W, bool SUM>
+__device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], f32x4 (&osum)[2], const bf16x8 (&pb)[2][2],
+                                        const lds_char* vt, const LaneAddr<DK, DV, W>& la) {
   constexpr int ROW = SwzTile<DV>::ROW;
+  if (SUM) {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      osum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[kt][0], osum[0], 0, 0, 0);
+      osum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[kt][1], osum[1], 0, 0, 0);
+    }
+  }
   // k-step outermost: consecutive MFMAs feed different accumulators
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -286,7 +299,8 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[DV / 16][2], const bf16x8 (&p
 // Softmax of one tile in place: mask, running reference, exponentials and P
 // in bf16.  alpha[qb] receives the factor the value sums must be multiplied
 // by; the return value says whether any row of the wave moved its reference.
-template <bool MASK, bool BIAS, bool DROP>
+// VSUM: also sum the rounded weights here (st.lu, v_dot2 against ones).
+template <bool MASK, bool BIAS, bool DROP, bool VSUM>
 __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2], RowState& st, float (&alpha)[2],
                                              float c, int n0, const int (&row_lo)[2],
                                              const unsigned (&row_span)[2], const float* const (&brow)[2],
@@ -358,12 +372,12 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&s)[4][2], bf16x8 (&pb)[2][2
         }
         w[2 * h] = cvt_pk_bf16(p[0], p[1]);
         w[2 * h + 1] = cvt_pk_bf16(p[2], p[3]);
-        if (!DROP) usum = add_bf16_pair(w[2 * h + 1], add_bf16_pair(w[2 * h], usum));
+        if (VSUM) usum = add_bf16_pair(w[2 * h + 1], add_bf16_pair(w[2 * h], usum));
       }
       pb[kt][qb] = __builtin_bit_cast(bf16x8, w);
     }
     st.l[qb] = fmaf(alpha[qb], st.l[qb], psum);
-    if (!DROP) st.lu[qb] = fmaf(alpha[qb], st.lu[qb], usum);
+    if (VSUM) st.lu[qb] = fmaf(alpha[qb], st.lu[qb], usum);
   }
   return __builtin_amdgcn_ballot_w64(any_grow) != 0;
 }
@@ -386,6 +400,15 @@ struct FwdTile {
   LaneAddr<DK, DV, W> la;
   QFrag<DK> qf;
   f32x4 o[DV / 16][2];
+  // Without dropout O is divided by the sum of the rounded weights that
+  // multiply V.  Eight-wave work-groups take it on the matrix cores (osum,
+  // 4 more products per tile), four-wave ones on the vector ALU (st.lu):
+  // measured each way, 200 calls, the matrix cores were 1.5% faster on the
+  // prefill and long context (eight waves) and 0.7% slower on the
+  // sliding window (four).
+  static constexpr bool MSUM = !DROP && W == 8;
+  static constexpr bool VSUM = !DROP && W != 8;
+  f32x4 osum[2];
   RowState st;
   int wfirst, wlast;  // this wave's first and last query row (wlast < wfirst: none)
 
@@ -433,7 +456,7 @@ struct FwdTile {
     // smallest end.
     if (MASK && __builtin_amdgcn_readfirstlane(
                     (int)(key_lo(mr, wlast) <= n0 && key_end(mr, wfirst, klen) >= n0 + kBN))) {
-      grow = softmax_tile<false, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
+      grow = softmax_tile<false, BIAS, DROP, VSUM>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
                                              vec_bias != 0, g, zw, dsp.keep);
     } else {
       if (MASK) {
@@ -444,7 +467,7 @@ struct FwdTile {
           row_span[qb] = end > lo ? (unsigned)(end - lo) : 0u;
         }
       }
-      grow = softmax_tile<MASK, BIAS, DROP>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
+      grow = softmax_tile<MASK, BIAS, DROP, VSUM>(s, pb, st, alpha, c, n0, row_lo, row_span, brow, rvalid, nk,
                                             vec_bias != 0, g, zw, dsp.keep);
     }
     if (grow) {
@@ -453,8 +476,12 @@ struct FwdTile {
         o[d][0] *= alpha[0];
         o[d][1] *= alpha[1];
       }
+      if (MSUM) {
+        osum[0] *= alpha[0];
+        osum[1] *= alpha[1];
+      }
     }
-    pv_tile<DK, DV, W>(o, pb, vcur, la);
+    pv_tile<DK, DV, W, MSUM>(o, osum, pb, vcur, la);
     wait_loads();
     __syncthreads();
   }
@@ -581,6 +608,7 @@ __global__ __launch_bounds__(threads_of<W>(), 2) void fwd_bf16_fast_kernel(
   ft.st.m[0] = ft.st.m[1] = kNegInf;
   ft.st.l[0] = ft.st.l[1] = 0.f;
   ft.st.lu[0] = ft.st.lu[1] = 0.f;
+  ft.osum[0] = ft.osum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   wait_loads();
   __syncthreads();
   {
@@ -639,7 +667,7 @@ __global__ __launch_bounds__(threads_of<W>(), 2) void fwd_bf16_fast_kernel(
     // value instead of carrying the key's own rounding (up to 2^-9 of |v|).
     // lse keeps the sum of the unrounded weights.  With dropout the
     // divisor stays the unrounded sum of the undropped weights.
-    const float l_out = DROP ? l_tot : quad_sum(ft.st.lu[qb]);
+    const float l_out = DROP ? l_tot : (decltype(ft)::MSUM ? ft.osum[qb][0] : quad_sum(ft.st.lu[qb]));
     if (!ft.rvalid[qb]) continue;
     const bool nonempty = l_tot > 0.f;
     const float inv = nonempty ? (DROP ? drop_scale : 1.f) / l_out : 0.f;
