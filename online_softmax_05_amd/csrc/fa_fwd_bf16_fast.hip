@@ -733,15 +733,15 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 // context 1.7% faster, the dropout prefill equal, the 1024-key sliding
 // window 5% slower (its work-groups visit few tiles, so a work-group's start
 // and its masked edge tiles weigh more).  Eight are used for launches
-// without a left window, bias or dropout that still give at least two
-// work-groups per CU.
+// without a left window, bias or dropout whose query tiles fill more than
+// 128 rows and that still give at least two work-groups per CU.
 template <int DK, int DV>
 hipError_t launch_b(const FwdArgs& a, hipStream_t s) {
   if (a.keep_256 < 256)
     return a.bias ? launch_t<DK, DV, true, true, 4>(a, s) : launch_t<DK, DV, false, true, 4>(a, s);
   if (a.bias) return launch_t<DK, DV, true, false, 4>(a, s);
   const long long wg8 = (long long)((a.Nq + rows_of<8>() - 1) / rows_of<8>()) * a.B * a.H;
-  if (a.wl < 0 && wg8 >= 512) return launch_t<DK, DV, false, false, 8>(a, s);
+  if (a.wl < 0 && a.Nq > rows_of<4>() && wg8 >= 512) return launch_t<DK, DV, false, false, 8>(a, s);
   return launch_t<DK, DV, false, false, 4>(a, s);
 }
 
