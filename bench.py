@@ -91,14 +91,15 @@ KERNEL_SOURCES = {
     "decode_mq": ["online_softmax_05_amd/csrc/fa_decode_mq.hip", "online_softmax_05_amd/csrc/fa_tiles.h",
                   "online_softmax_05_amd/csrc/fa_common.h", "online_softmax_05_amd/csrc/fa_merge.h"],
 }
-# (the fast forward's last template argument is its waves per work-group)
+# (the last template argument of the fast forward and of the dK/dV kernel is
+# its waves per work-group)
 KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
                 "long": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
                 "window": "fwd_bf16_fast_kernel<128, 128, false, false, 4>",
                 "dropout": "fwd_bf16_fast_kernel<128, 128, false, true, 4>",
-                "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true> + bwd_dkdv_bf16_kernel<128, 128, false, true>",
+                "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true> + bwd_dkdv_bf16_kernel<128, 128, false, true, 4>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
-                "backward": "bwd_dq_bf16_kernel<128, 128, false, false> + bwd_dkdv_bf16_kernel<128, 128, false, false>",
+                "backward": "bwd_dq_bf16_kernel<128, 128, false, false> + bwd_dkdv_bf16_kernel<128, 128, false, false, 8>",
                 "decode_mq": "mq_partial_bf16_kernel + mq_merge_kernel"}
 
 

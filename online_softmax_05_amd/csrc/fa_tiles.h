@@ -42,20 +42,23 @@ __device__ __forceinline__ int swz(int row) {
   return row & 7;
 }
 
-template <int D>
+// W: the waves that load a tile together (kWaves unless a kernel says
+// otherwise)
+template <int D, int W = kWaves>
 struct Tile {
   static constexpr int R = D / 8;   // 16-byte chunks per row
   static constexpr int ROW = R * 16;
   static constexpr int BYTES = kTile * ROW;
-  static constexpr int IPW = kTile * R / 64 / kWaves;  // 1 KiB direct loads per wave
+  static constexpr int IPW = kTile * R / 64 / W;  // 1 KiB direct loads per wave
+  static_assert(IPW >= 1 && kTile * R % (64 * W) == 0, "tile shape");
 };
 
 // Per-lane address parts for one tile layout D.
-template <int D>
+template <int D, int W = kWaves>
 struct TileAddr {
   int frag[D / 32];  // operand read (tile row 16blk + r16, dims 32t + 8g .. +7): + 16 blk ROW
   int tr[D / 16];    // transposed read of dim block db (tile rows 32kt + 16h + 4g + e): + (32kt + 16h) ROW
-  int ld[Tile<D>::IPW];  // byte offset in the tile of each of this wave's direct loads
+  int ld[Tile<D, W>::IPW];  // byte offset in the tile of each of this wave's direct loads
 
   __device__ __forceinline__ void init(int lane, int wave) {
     constexpr int ROW = Tile<D>::ROW;
@@ -66,8 +69,8 @@ struct TileAddr {
     for (int db = 0; db < D / 16; ++db)
       tr[db] = (4 * g + e) * ROW + 16 * ((2 * db + (r >> 1)) ^ swz<D>(4 * g + e)) + 8 * (r & 1);
 #pragma unroll
-    for (int i = 0; i < Tile<D>::IPW; ++i) {
-      const int slot = (wave * Tile<D>::IPW + i) * 64 + lane;
+    for (int i = 0; i < Tile<D, W>::IPW; ++i) {
+      const int slot = (wave * Tile<D, W>::IPW + i) * 64 + lane;
       const int row = slot / Tile<D>::R;
       ld[i] = 2 * (row * D + ((slot % Tile<D>::R) ^ swz<D>(row)) * 8);
     }
@@ -92,9 +95,9 @@ __device__ __forceinline__ HeadBuf head_buf(const uint16_t* base, uint32_t bytes
 // masked; zero rows add nothing to the products).  CPOL is the cache policy:
 // 0, or kNonTemporal for data read once per call.
 constexpr int kNonTemporal = 2;
-template <int D, int CPOL = 0>
+template <int D, int CPOL = 0, int W = kWaves>
 __device__ __forceinline__ void load_tile(const HeadBuf& b, int row0, const int* ld, lds_char* dst, int wave) {
-  constexpr int IPW = Tile<D>::IPW;
+  constexpr int IPW = Tile<D, W>::IPW;
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
