@@ -49,7 +49,8 @@ cpu_baseline times the float64 oracle (test infrastructure, used here only
 for this leg) on a bounded sample of the same workload on the host cores;
 max_abs_err compares the GPU outputs of the timed launches with the oracle on
 that same sample (o and lse max-abs; gradients max-abs over the largest
-reference entry).
+reference entry).  The oracle samples run after every workload has been
+timed, so that no host work overlaps a timed region.
 """
 
 import argparse
@@ -415,14 +416,14 @@ def run_prefill(name, args, dev):
                     allowed_pairs=pairs, **({} if wl is None else {"window_left": wl}),
                     **({} if keep == 256 else {"dropout_keep_256": keep, "dropout_seed": seed})),
     )
-    if not args.no_cpu_baseline:
-        log(f"{name}: timing the oracle on a bounded sample")
-        res["cpu_baseline"], err = cpu_baseline_prefill(inp, name, args.cpu_budget, out, lse)
-        res["cpu_baseline"]["value_same_unit_as_gpu"] = True
-        res["max_abs_err"] = _err_fields(err)
-    del inp, out, lse
-    torch.cuda.empty_cache()
-    return res
+    def finish():
+        if not args.no_cpu_baseline:
+            log(f"{name}: timing the oracle on a bounded sample")
+            res["cpu_baseline"], err = cpu_baseline_prefill(inp, name, args.cpu_budget, out, lse)
+            res["cpu_baseline"]["value_same_unit_as_gpu"] = True
+            res["max_abs_err"] = _err_fields(err)
+
+    return res, finish
 
 
 def cpu_baseline_backward(inp, budget_s, grads, name="backward"):
@@ -498,12 +499,13 @@ def run_backward(args, dev, name="backward"):
                     dtype="bf16", allowed_pairs=pairs,
                     **({} if keep == 256 else {"dropout_keep_256": keep, "dropout_seed": seed})),
     )
-    if not args.no_cpu_baseline:
-        log(f"{name}: timing the oracle on a bounded sample")
-        res["cpu_baseline"], res["max_abs_err"] = cpu_baseline_backward(inp, args.cpu_budget, (dq, dk_, dv_), name)
-    del inp, o, lse, dq, dk_, dv_, ws
-    torch.cuda.empty_cache()
-    return res
+    def finish():
+        if not args.no_cpu_baseline:
+            log(f"{name}: timing the oracle on a bounded sample")
+            res["cpu_baseline"], res["max_abs_err"] = cpu_baseline_backward(inp, args.cpu_budget, (dq, dk_, dv_),
+                                                                            name)
+
+    return res, finish
 
 
 def run_decode_mq(args, dev):
@@ -541,13 +543,13 @@ def run_decode_mq(args, dev):
         config=dict(workload=workloads.DESCRIPTIONS["decode_mq"], B=B, H=H, Nq=Nq, Nk_max=Nk, dk=dk, dv=dv,
                     chunk=chunk, causal=True, dtype="bf16", k_len_sum=int(kl.sum().item())),
     )
-    if not args.no_cpu_baseline:
-        log("decode_mq: timing the oracle on a bounded sample")
-        res["cpu_baseline"], err = cpu_baseline_decode(inp, args.cpu_budget, out, lse, nq=Nq, name="decode_mq")
-        res["max_abs_err"] = _err_fields(err)
-    del inp, out, lse, ws
-    torch.cuda.empty_cache()
-    return res
+    def finish():
+        if not args.no_cpu_baseline:
+            log("decode_mq: timing the oracle on a bounded sample")
+            res["cpu_baseline"], err = cpu_baseline_decode(inp, args.cpu_budget, out, lse, nq=Nq, name="decode_mq")
+            res["max_abs_err"] = _err_fields(err)
+
+    return res, finish
 
 
 def run_decode(args, dev):
@@ -585,13 +587,13 @@ def run_decode(args, dev):
         config=dict(workload=workloads.DESCRIPTIONS["decode"], B=B, H=H, Nk_max=Nk, dk=dk, dv=dv, chunk=chunk,
                     dtype="bf16", k_len_sum=int(kl.sum().item())),
     )
-    if not args.no_cpu_baseline:
-        log("decode: timing the oracle on a bounded sample")
-        res["cpu_baseline"], err = cpu_baseline_decode(inp, args.cpu_budget, out, lse)
-        res["max_abs_err"] = _err_fields(err)
-    del inp, out, lse, ws
-    torch.cuda.empty_cache()
-    return res
+    def finish():
+        if not args.no_cpu_baseline:
+            log("decode: timing the oracle on a bounded sample")
+            res["cpu_baseline"], err = cpu_baseline_decode(inp, args.cpu_budget, out, lse)
+            res["max_abs_err"] = _err_fields(err)
+
+    return res, finish
 
 
 def run_small(name, args, dev):
@@ -652,7 +654,10 @@ def run_small(name, args, dev):
                     allowed_pairs=pairs, **({} if inp["k_len"] is None else {"k_len": inp["k_len"].tolist()}),
                     bias=inp["bias"] is not None),
     )
-    if not args.no_cpu_baseline:
+
+    def finish():
+        if args.no_cpu_baseline:
+            return
         log(f"{name}: timing the oracle on the whole workload")
         kl = None if inp["k_len"] is None else inp["k_len"].numpy()
         args64 = [inp[x].double().numpy() for x in ("q", "k", "v")]
@@ -673,7 +678,8 @@ def run_small(name, args, dev):
         lg = lse.double().cpu().numpy().reshape(-1)
         _err_update(err, og, lg, o_ref.reshape(-1, dv), l_ref.reshape(-1))
         res["max_abs_err"] = _err_fields(err)
-    return res
+
+    return res, finish
 
 
 def copy_calibration(dev, nbytes=1 << 30, reps=5):
@@ -724,9 +730,17 @@ def main():
                "dropout_bwd": lambda a, d: run_backward(a, d, "dropout_bwd"),
                "small": lambda a, d: run_small("small", a, d), "masks_f32": lambda a, d: run_small("masks_f32", a, d),
                "masks_bf16": lambda a, d: run_small("masks_bf16", a, d)}
-    results = {}
+    # Every workload is timed first; the oracle samples (CPU baselines and
+    # error figures) run afterwards, on the outputs each timed run left, so
+    # that no host-side work -- nor the BLAS worker threads it leaves
+    # spinning -- overlaps any GPU timing.
+    results, pending = {}, []
     for w in order:
-        results[w] = runners[w](args, dev) if w in runners else run_prefill(w, args, dev)
+        results[w], finish = runners[w](args, dev) if w in runners else run_prefill(w, args, dev)
+        pending.append(finish)
+    for finish in pending:
+        finish()
+    pending.clear()
 
     main_res = results[args.workload]
     line = {
