@@ -98,9 +98,9 @@ KERNEL_NAMES = {"prefill": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
                 "long": "fwd_bf16_fast_kernel<128, 128, false, false, 8>",
                 "window": "fwd_bf16_fast_kernel<128, 128, false, false, 4>",
                 "dropout": "fwd_bf16_fast_kernel<128, 128, false, true, 4>",
-                "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true> + bwd_dkdv_bf16_kernel<128, 128, false, true, 4>",
+                "dropout_bwd": "bwd_dq_bf16_kernel<128, 128, false, true, 4> + bwd_dkdv_bf16_kernel<128, 128, false, true, 4>",
                 "decode": "decode_partial_fast_kernel + decode_merge_kernel",
-                "backward": "bwd_dq_bf16_kernel<128, 128, false, false> + bwd_dkdv_bf16_kernel<128, 128, false, false, 8>",
+                "backward": "bwd_dq_bf16_kernel<128, 128, false, false, 8> + bwd_dkdv_bf16_kernel<128, 128, false, false, 8>",
                 "decode_mq": "mq_partial_bf16_kernel + mq_merge_kernel"}
 
 

@@ -15,7 +15,8 @@
 // follows on the same stream.  Neither uses atomics, so the results are
 // bitwise reproducible.
 //
-// dQ kernel: one work-group = 4 waves = 128 query rows of one (batch, head),
+// dQ kernel: one work-group = 8 waves = 256 query rows of one (batch, head)
+// (4 waves = 128 rows with a bias or dropout),
 // 32 rows per wave (two 16-row blocks, so that every K or V fragment read
 // from LDS feeds two products) with their Q and G rows held as MFMA
 // operands.  Key tiles
@@ -61,12 +62,9 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 64 * tiles::kWaves;
-
 using tiles::HeadBuf;
 using tiles::head_buf;
 using tiles::kTile;
-using tiles::kWaves;
 using tiles::Tile;
 using tiles::TileAddr;
 using tiles::lds_char;
@@ -105,10 +103,8 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
 // dQ
 // ---------------------------------------------------------------------------
 
-constexpr int kDqRows = 32 * kWaves;  // query rows per dQ work-group (32 per wave)
-
-template <int DK, int DV, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
+template <int DK, int DV, bool BIAS, bool DROP, int W>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ cvec,
@@ -126,6 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   lds_char* const V0 = (lds_char*)vb0;
   lds_char* const V1 = (lds_char*)vb1;
 
+  constexpr int kDqRows = 32 * W;  // query rows per work-group (32 per wave)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -138,8 +135,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
   const int q0 = tc.qt * kDqRows;
   const int klen = clamp_klen(k_len, b, Nk);
 
-  TileAddr<DK> ka;
-  TileAddr<DV> va;
+  TileAddr<DK, W> ka;
+  TileAddr<DV, W> va;
   ka.init(lane, wave);
   va.init(lane, wave);
   // rows at or past the key length read as zeros (never from memory)
@@ -213,8 +210,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     __syncthreads();  // tile t visible; tile t-1's buffers free
     const int j0 = t * kTile;
     if (t + 1 < t_end) {
-      load_tile<DK>(kh, j0 + kTile, ka.ld, kn, wave);
-      load_tile<DV>(vh, j0 + kTile, va.ld, vn, wave);
+      load_tile<DK, 0, W>(kh, j0 + kTile, ka.ld, kn, wave);
+      load_tile<DV, 0, W>(vh, j0 + kTile, va.ld, vn, wave);
     }
     // a masked tile that none of this wave's rows can see adds nothing to
     // dQ (all its P are zero): skip its products (the row ranges only grow
@@ -283,8 +280,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_kernel(
     }
   };
   if (t_begin < t_end) {
-    load_tile<DK>(kh, t_begin * kTile, ka.ld, K0, wave);
-    load_tile<DV>(vh, t_begin * kTile, va.ld, V0, wave);
+    load_tile<DK, 0, W>(kh, t_begin * kTile, ka.ld, K0, wave);
+    load_tile<DV, 0, W>(vh, t_begin * kTile, va.ld, V0, wave);
   }
   // Tile t sits in buffer (t - t_begin) & 1.  Tiles [t_full, t_full_end)
   // need no mask (unless there is a bias, or a row of the wave is past Nq
@@ -615,9 +612,14 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const float drop_scale = 256.f / (float)a.keep_256;
   const unsigned bh = (unsigned)(a.B * a.H);
   // dQ first: it stores c for the dK/dV kernel
+  // eight waves (256 query rows) per dQ work-group halve the K/V tile loads
+  // per product for the plain instance: 1.875 against 1.892 ms per backward
+  // call (100 calls x 3, same box)
+  constexpr int QW = (BIAS || DROP) ? 4 : 8;
   if ((long long)a.B * a.H * a.Nq > 0)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP>), dim3((unsigned)((a.Nq + kDqRows - 1) / kDqRows) * bh),
-                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<DK, DV, BIAS, DROP, QW>),
+                       dim3((unsigned)((a.Nq + 32 * QW - 1) / (32 * QW)) * bh), dim3(64 * QW), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ws_c, a.bias, a.k_len,
                        (uint16_t*)a.dq_out, a.H, a.Nq, a.Nk, a.scale, mr, dsp, drop_scale);
   if (a.Nk > 0)
