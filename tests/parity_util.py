@@ -167,3 +167,47 @@ def compare_every_head(o_gpu, lse_gpu, q, k, v, *, scale, causal, k_len_host=Non
     assert err_o <= tol["o"], f"{what}: max |o - o_ref| = {err_o:.3e} > {tol['o']}"
     assert err_l <= tol["lse"], f"{what}: max |lse - lse_ref| = {err_l:.3e} > {tol['lse']}"
     return err_o, err_l, B * H * Nq
+
+
+def bwd_every_head(q, k, v, g, o, lse, grads, *, scale, causal, tol, what, dropout=None, floor=False,
+                   workers=8):
+    """Every element of dQ, dK and dV of a full-size backward against the oracle.
+
+    The oracle rebuilds P of each (batch, head) from the GPU forward's o and
+    lse (the backward's own inputs) and returns the head's three gradients;
+    heads run ``workers`` at a time on host threads with one BLAS thread each.
+    A head's error in a gradient is max |got - ref| over the head, relative
+    to max |ref| over the head (or, with ``floor``, to at least one term of
+    the gradient sums, scale * |g| * |v| * max(|q|, |k|), for gradients that
+    cancel to near zero).  Asserts the worst head of each gradient against
+    ``tol`` and returns the three worst relative errors."""
+    import concurrent.futures
+
+    host = [t.detach().to("cpu") for t in (q, k, v, g, o, lse, *grads)]
+    qh, kh, vh, gh, oh, lh, dqh, dkh, dvh = host
+    B, H, Nq = qh.shape[0], qh.shape[1], qh.shape[2]
+    sc = scale32(scale)
+
+    def head(bh):
+        b, h = divmod(bh, H)
+        qq, kk, vv, gg = (t[b, h].double().numpy() for t in (qh, kh, vh, gh))
+        ref = oracle.attention_bwd_head(qq, kk, vv, gg, scale=sc, nq=Nq, causal=causal, o=oh[b, h].double().numpy(),
+                                        lse=lh[b, h].double().numpy(), dropout=dropout, bh=bh)
+        fl = abs(sc) * np.abs(gg).max() * np.abs(vv).max() * max(np.abs(qq).max(), np.abs(kk).max()) if floor else 0.0
+        errs = []
+        for got_t, r in zip((dqh, dkh, dvh), ref):
+            got = got_t[b, h].double().numpy()
+            assert not np.isnan(got).any(), f"{what}: NaN in a gradient of ({b}, {h})"
+            errs.append(float(np.max(np.abs(got - r))) / max(float(np.max(np.abs(r))), fl, 1e-30))
+        return errs
+
+    worst = [0.0, 0.0, 0.0]
+    with _blas_limit(1), concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for i, errs in enumerate(ex.map(head, range(B * H))):
+            worst = [max(a, e) for a, e in zip(worst, errs)]
+            if (i + 1) % 16 == 0 or i + 1 == B * H:
+                say(f"{what}: {i + 1} of {B * H} heads, worst rel err dQ {worst[0]:.2e} dK {worst[1]:.2e} "
+                    f"dV {worst[2]:.2e} (tol {tol:.0e})")
+    for name, e in zip(("dQ", "dK", "dV"), worst):
+        assert e <= tol, f"{what}: {name} relative error {e:.3e} > {tol}"
+    return worst

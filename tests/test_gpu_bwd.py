@@ -28,7 +28,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity_util import f64, say, scale32
+from tests.parity_util import bwd_every_head, f64, say, scale32
 
 pytestmark = pytest.mark.gpu
 
@@ -154,26 +154,17 @@ def test_bwd_deterministic(dev):
         assert torch.equal(x, y)
 
 
-def test_bwd_full_size_sampled_heads(dev):
+def test_bwd_full_size_every_head(dev):
     """The benchmark's backward workload (causal bf16 4x32x4096^2, d = 128),
-    in the launch configuration the benchmark times; two (batch, head) pairs
-    are recomputed in full by the oracle from the GPU forward's O and lse."""
+    in the launch configuration the benchmark times: every element of dQ, dK
+    and dV of all 128 (batch, head) pairs against the oracle, which rebuilds
+    P from the GPU forward's O and lse."""
     import online_softmax_05_amd as fa
 
     say("bwd full size: drawing the backward workload")
     inp = workloads.backward(dev)
     o, lse = fa.fa_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True)
-    dq, dk, dv = fa.fa_bwd(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True)
+    grads = fa.fa_bwd(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, scale=inp["scale"], causal=True)
     torch.cuda.synchronize()
-    N = inp["q"].shape[2]
-    for b, h in ((0, 0), (3, 31)):
-        say(f"bwd full size: oracle for head ({b}, {h})")
-        ref = oracle.attention_bwd_head(f64(inp["q"][b, h]), f64(inp["k"][b, h]), f64(inp["v"][b, h]),
-                                        f64(inp["g"][b, h]), scale=scale32(inp["scale"]), nq=N, causal=True,
-                                        o=f64(o[b, h]), lse=f64(lse[b, h]))
-        floor = term_size({"scale": inp["scale"], "q": inp["q"][b, h], "k": inp["k"][b, h], "v": inp["v"][b, h]},
-                          inp["g"][b, h])
-        for name, x, r in zip(("dQ", "dK", "dV"), (dq[b, h], dk[b, h], dv[b, h]), ref):
-            e = rel_err(x, r, floor)
-            say(f"bwd full size head ({b}, {h}) {name}: rel err {e:.2e} (tol {TOL[torch.bfloat16]:.0e})")
-            assert e <= TOL[torch.bfloat16]
+    bwd_every_head(inp["q"], inp["k"], inp["v"], inp["g"], o, lse, grads, scale=inp["scale"], causal=True,
+                   tol=TOL[torch.bfloat16], what="bwd full size", floor=True)

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity_util import TOL, compare, compare_every_head, f64, oracle_full, say, scale32
+from tests.parity_util import bwd_every_head, TOL, compare, compare_every_head, f64, oracle_full, say, scale32
 
 pytestmark = pytest.mark.gpu
 
@@ -236,25 +236,18 @@ def test_backward_ex_defaults_match_fa_bwd(dev):
         assert torch.equal(x, y)
 
 
-def test_backward_dropout_full_size_sampled_heads(dev):
+def test_backward_dropout_full_size_every_head(dev):
     """The prefill shape with dropout p = 0.1 through fa_fwd_ex and fa_bwd_ex:
-    two whole heads' gradients against the oracle (given the GPU's O and
-    lse)."""
+    every element of dQ, dK and dV of all 128 heads against the oracle (given
+    the GPU's O and lse)."""
     import online_softmax_05_amd as fa
 
     inp = workloads.backward(dev)
     keep, seed = 230, 77
     say("bwd dropout full size 4x32x4096 d128 bf16 keep 230")
     o, lse = fa.fa_fwd_ex(inp["q"], inp["k"], inp["v"], causal=True, keep_256=keep, seed=seed, scale=inp["scale"])
-    dq, dk, dv = fa.fa_bwd_ex(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, causal=True, keep_256=keep, seed=seed,
-                              scale=inp["scale"])
+    grads = fa.fa_bwd_ex(inp["q"], inp["k"], inp["v"], o, inp["g"], lse, causal=True, keep_256=keep, seed=seed,
+                         scale=inp["scale"])
     torch.cuda.synchronize()
-    H = inp["q"].shape[1]
-    for b, h in ((0, 0), (3, 31)):
-        ref = oracle.attention_bwd_head(f64(inp["q"][b, h]), f64(inp["k"][b, h]), f64(inp["v"][b, h]),
-                                        f64(inp["g"][b, h]), scale=scale32(inp["scale"]), nq=4096, causal=True,
-                                        o=f64(o[b, h]), lse=f64(lse[b, h]), dropout=(keep, seed), bh=b * H + h)
-        for name, x, r in zip(("dQ", "dK", "dV"), (dq[b, h], dk[b, h], dv[b, h]), ref):
-            e = float(np.max(np.abs(f64(x) - r))) / float(np.max(np.abs(r)))
-            say(f"full-size dropout bwd head ({b},{h}) {name}: rel err {e:.2e}")
-            assert e <= BWD_TOL[torch.bfloat16], (b, h, name, e)
+    bwd_every_head(inp["q"], inp["k"], inp["v"], inp["g"], o, lse, grads, scale=inp["scale"], causal=True,
+                   tol=BWD_TOL[torch.bfloat16], what="full-size dropout bwd", dropout=(keep, seed))
