@@ -106,6 +106,9 @@ CASES = [
     (2, 1, 33, 65, 128, 64, False, True, [0, 50]),     # an all-empty sequence
     (1, 1, 1, 1, 16, 8, False, False, None),
     (1, 1, 5, 300, 32, 96, True, False, "random"),
+    # bf16: several 256-row dQ and 128-key dK/dV work-groups, both axes ragged
+    (2, 2, 600, 700, 128, 128, True, False, "random"),
+    (1, 3, 513, 390, 64, 128, False, False, [389]),   # one row past two dQ work-groups; keys end mid-group
 ]
 
 
