@@ -199,6 +199,19 @@ def decode_mq(device):
     return inp
 
 
+def long_cache(device, Nk=9_000_000, nq=4, seed=17):
+    """One sequence and head whose K and V caches each span more than 2^31
+    bytes (9e6 keys of d = 128 in bf16: 2.3 GB each), drawn on the device:
+    q [1,1,nq,128] and caches [1,1,Nk,128] ~ N(0, 1), the key length 3 keys
+    short of Nk."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = _randn_dev(g, (1, 1, nq, 128), device, torch.bfloat16)
+    k = _randn_dev(g, (1, 1, Nk, 128), device, torch.bfloat16)
+    v = _randn_dev(g, (1, 1, Nk, 128), device, torch.bfloat16)
+    k_len = torch.tensor([Nk - 3], dtype=torch.int32)
+    return dict(q=q, k=k, v=v, k_len=k_len, scale=1.0 / math.sqrt(128))
+
+
 def to_device(inputs, device):
     """Copy every tensor of a CPU-drawn workload to ``device``."""
     out = {}
