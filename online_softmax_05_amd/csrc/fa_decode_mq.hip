@@ -381,8 +381,11 @@ hipError_t launch_mq(const DecodeMqArgs& a, hipStream_t stream, bool mfma) {
 
 hipError_t launch_decode_mq_bf16(const DecodeMqArgs& a, hipStream_t s) {
   const auto aligned = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  // each chunk's K and V rows are read through buffer descriptors of their
+  // own (64-bit base at the chunk), so only one chunk must fit their 31-bit
+  // byte range, not the whole head
   const bool mfma = a.dk == kD && a.dv == kD && aligned(a.q) && aligned(a.k) && aligned(a.v) &&
-                    tiles::head_fits(a.Nk, kD);  // K/V tiles are read with buffer loads
+                    tiles::head_fits(a.chunk < a.Nk ? a.chunk : a.Nk, kD);
   return launch_mq<uint16_t>(a, s, mfma);
 }
 hipError_t launch_decode_mq_f32(const DecodeMqArgs& a, hipStream_t s) { return launch_mq<float>(a, s, false); }
